@@ -1,0 +1,419 @@
+"""CPU oracle for one tensor-parallel rank's share of a transformer block's linear layers.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg may import this module.  The GPU library never calls it and
+shares no code, header, table or constant generator with it.
+
+Everything here is the plain definition of what the hot path computes, written
+out in numpy float64 from exactly widened bf16 / E4M3 inputs, then rounded once
+where the method rounds.  A library primitive (numpy's float64 matmul, scipy's
+double-precision ``erf``) serves as a step; there is no blocking, fusion or
+reordering beyond the definitions.  Sources (web pages):
+
+  [nanotron]  nanotron rules page "Tensor-Parallel Component Patterns",
+              sections "Attention Module" and "MLP Module".
+  [deepspeed] DeepSpeed ``deepspeed/module_inject/layers.py``, class
+              ``SubParamLinearLayer`` (its docstring, ``__init__``, ``forward``).
+  [palm]      google-research ``scaling_transformer_inference_efficiency/
+              layers/two_d_parallel_xmap.py``: ``allgather_layernorm``,
+              ``unembed_manual``, ``transformer_layer_weight_gathered``.
+  [tt]        Tenstorrent ``models/common/modules/lm_head/lm_head_1d.py``:
+              module docstring, ``LMHead1DConfig``, ``LMHead1D.forward``,
+              ``LMHead1D.from_model_args``.
+  [cerebras]  "Cerebras Modelzoo Layers" API page, ``Transformer`` parameters.
+
+Notation: ``bf16(v)`` rounds a float32 to bf16 (nearest, ties to even);
+``f32(v)`` rounds a float64 to float32 (nearest, ties to even).  Inputs arrive
+as bf16 / E4M3 bit patterns (``uint16`` / ``uint8``).  Where the pages leave a
+step open, the reading taken is stated at the function.
+
+Parity pins: every function here is checked by the CPU tests against brute
+force, closed forms, invariants or library routines (see ``tests/test_oracle_*``).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+RMS_EPS = 1e-6
+FP8_BLOCK = 128
+
+ACT_NONE, ACT_GELU = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+LAYOUT_LOCAL, LAYOUT_LOGICAL = 0, 1
+
+
+# --------------------------------------------------------------------------------------
+# Codecs
+# --------------------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (bf16 is the top half of a float32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f32(v) -> np.ndarray:
+    """Round float64 to float32, nearest-even (numpy's cast)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32)
+
+
+def bf16_round(v32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 bit patterns, nearest with ties to even.
+
+    bf16 keeps the top 16 bits of the float32 pattern; the 16 dropped bits are
+    compared with half an ulp (0x8000) and ties go to the even kept pattern.
+    NaN maps to the quiet NaN 0x7FC0; overflow rounds to infinity as the
+    pattern arithmetic carries into the exponent.
+    """
+    a = np.ascontiguousarray(v32, dtype=np.float32)
+    u = a.view(np.uint32)
+    keep = (u >> np.uint32(16)).astype(np.uint32)
+    rest = u & np.uint32(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint32(1)) == 1))
+    out = (keep + up.astype(np.uint32)).astype(np.uint16)
+    out = np.where(np.isnan(a), np.uint16(0x7FC0), out).astype(np.uint16)
+    return out
+
+
+def e4m3_table() -> np.ndarray:
+    """Value of every OCP 8-bit E4M3FN code, from the format's definition.
+
+    Layout s.eeee.mmm with exponent bias 7: a normal code is
+    (-1)^s * (1 + m/8) * 2^(e-7); e = 0 gives the subnormals (-1)^s * (m/8) * 2^-6;
+    the codes with e = 15 and m = 7 (0x7F, 0xFF) are NaN; there are no infinities,
+    so 0x7E = 448 is the largest finite value.  (The page's ``lm_head_dtype``
+    is an 8-bit block format; the E4M3FN reading is stated where it is used.)
+    """
+    t = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        s = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            t[code] = np.nan
+        elif e == 0:
+            t[code] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            t[code] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return t
+
+
+_E4M3 = e4m3_table()
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+# --------------------------------------------------------------------------------------
+# O1 - shard widths  [deepspeed] __init__; [nanotron] local dims; [tt] from_model_args
+# --------------------------------------------------------------------------------------
+
+def shard_widths(subparam_sizes, tp_size: int, rank: int):
+    """Per-sub-parameter widths and offsets of rank ``rank`` of ``tp_size``.
+
+    [deepspeed] ``SubParamLinearLayer`` views a weight's output dimension as
+    several logical sub-parameters (e.g. q, k, v) and partitions *each one*
+    separately along the output dimension; the widths are resolved once per
+    model.  [nanotron] uses ``n // tp`` for evenly divisible dimensions.
+
+    Reading for a size that ``tp_size`` does not divide (the page gives no body
+    for its width function): a balanced split whose remainder goes to the lowest
+    ranks, ``w_s(r) = S_s // tp + (r < S_s % tp)``; a sub-parameter smaller than
+    ``tp_size`` is rejected.
+
+    Returns ``(width, logical_off, local_off, total)``: lists over sub-params of
+    the rank's width, the first logical output row it owns, the first row inside
+    the rank's materialised shard, and the shard's total rows.  The shard is the
+    concatenation, in sub-parameter order, of the logical row ranges
+    ``[logical_off[s], logical_off[s] + width[s])``.
+    """
+    sizes = [int(s) for s in subparam_sizes]
+    if tp_size < 1:
+        raise ValueError(f"tp_size must be >= 1, got {tp_size}")
+    if not 0 <= rank < tp_size:
+        raise ValueError(f"rank {rank} outside [0, {tp_size})")
+    if len(sizes) < 1:
+        raise ValueError("at least one sub-parameter size is required")
+    for s in sizes:
+        if s < tp_size:
+            raise ValueError(f"sub-parameter size {s} is smaller than tp_size {tp_size}")
+
+    def w(size, r):
+        return size // tp_size + (1 if r < size % tp_size else 0)
+
+    width, logical_off, local_off = [], [], []
+    base = 0
+    local = 0
+    for size in sizes:
+        width.append(w(size, rank))
+        logical_off.append(base + sum(w(size, q) for q in range(rank)))
+        local_off.append(local)
+        local += width[-1]
+        base += size
+    return width, logical_off, local_off, local
+
+
+def shard_rows(subparam_sizes, tp_size: int, rank: int) -> np.ndarray:
+    """Logical output rows held by the rank's shard, in shard order."""
+    width, loff, _, _ = shard_widths(subparam_sizes, tp_size, rank)
+    return np.concatenate([np.arange(o, o + w) for w, o in zip(width, loff)]).astype(np.int64)
+
+
+def take_column_shard(w_logical: np.ndarray, subparam_sizes, tp_size: int, rank: int) -> np.ndarray:
+    """Materialise a rank's column shard (rows of ``[N_logical, K]``), as done once at load."""
+    return np.ascontiguousarray(w_logical[shard_rows(subparam_sizes, tp_size, rank)])
+
+
+def take_row_shard(w_logical: np.ndarray, tp_size: int, rank: int) -> np.ndarray:
+    """A rank's row-parallel shard: columns of ``[N, K_logical]`` (the input dim is split)."""
+    rows = shard_rows([w_logical.shape[1]], tp_size, rank)
+    return np.ascontiguousarray(w_logical[:, rows])
+
+
+# --------------------------------------------------------------------------------------
+# O2 - column-parallel linear  [deepspeed] forward; [nanotron] MLP c_fc + F.gelu
+# --------------------------------------------------------------------------------------
+
+def gelu_erf(a32: np.ndarray) -> np.ndarray:
+    """Exact (erf) GELU of float32 values, evaluated in double: 0.5 a (1 + erf(a / sqrt 2)).
+
+    [nanotron] applies ``F.gelu`` between ``c_fc`` and ``c_proj``; ``F.gelu``'s
+    default and [cerebras] ``Transformer(activation='gelu')`` are the erf form.
+    """
+    a = np.asarray(a32, dtype=np.float64)
+    return 0.5 * a * (1.0 + _erf(a / math.sqrt(2.0)))
+
+
+def column_linear(x_bits, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size, rank,
+                  act=ACT_NONE, out_dtype=OUT_BF16, layout=LAYOUT_LOCAL, n_logical=None):
+    """One rank's column-parallel linear with sub-parameter sharding.
+
+    [deepspeed] forward: ``output = input @ weight.T`` then ``+ bias``, on the
+    rank's materialised shard (weight rows and bias entries of the rank's slice
+    of every sub-parameter); the input is replicated across ranks.
+    [nanotron] ``MLP``: ``c_fc`` output keeps ``intermediate // tp`` columns,
+    then ``F.gelu``.
+
+    Per output element: ``acc = sum_k x[m,k] W_r[j,k] + b_r[j]`` (float64), then
+    ``a = f32(acc)``; with GELU ``a = f32(gelu(a))`` -- one rounding of the
+    fused result to the output type (reading: the activation is applied to the
+    float32 accumulator, then rounded once).  Output ``bf16(a)`` (uint16 bits)
+    or ``a`` (float32).
+
+    ``layout=LAYOUT_LOCAL`` returns ``[M, N_r]``.  ``LAYOUT_LOGICAL`` returns the
+    rank's columns placed at their logical positions in ``[M, n_logical]`` and a
+    boolean mask of the columns this rank wrote (the others are untouched).
+    """
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_shard_bits)
+    width, loff, lcl, total = shard_widths(subparam_sizes, tp_size, rank)
+    if w.shape[0] != total:
+        raise ValueError(f"weight shard has {w.shape[0]} rows, shard total is {total}")
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x and weight K differ")
+    acc = x @ w.T
+    if bias_shard_bits is not None:
+        b = bf16_to_f64(bias_shard_bits)
+        if b.shape != (total,):
+            raise ValueError(f"bias shard has {b.size} entries, expected {total}")
+        acc = acc + b[None, :]
+    a = f32(acc)
+    if act == ACT_GELU:
+        a = f32(gelu_erf(a))
+    y = bf16_round(a) if out_dtype == OUT_BF16 else a
+    if layout == LAYOUT_LOCAL:
+        return y
+    if n_logical is None:
+        n_logical = sum(int(s) for s in subparam_sizes)
+    out = np.zeros((y.shape[0], n_logical), dtype=y.dtype)
+    mask = np.zeros(n_logical, dtype=bool)
+    for wd, lo, lc in zip(width, loff, lcl):
+        out[:, lo:lo + wd] = y[:, lc:lc + wd]
+        mask[lo:lo + wd] = True
+    return out, mask
+
+
+# --------------------------------------------------------------------------------------
+# O3 - row-parallel partial  [nanotron] MLP c_proj / Attention c_proj
+# --------------------------------------------------------------------------------------
+
+def row_linear_partial(x_shard_bits, w_shard_bits, bias_bits=None, rank=0, y_prev=None):
+    """One rank's row-parallel partial sum, float32, before any reduction.
+
+    [nanotron] ``TensorParallelRowLinear(intermediate, hidden)``: each rank holds
+    the input columns ``K_r`` of its shard and the matching weight columns, and
+    its product is a partial of the full output; the pages reduce the partials
+    with a collective afterwards.  ``P_r[m,n] = f32(sum_{k<K_r} x_r[m,k] W_r[n,k])``.
+
+    Reading for the bias (the pages' row layers use ``bias=False``): only rank 0
+    adds it, so that the sum over ranks equals the unsharded output.  With
+    ``y_prev`` the partial is added to an existing float32 buffer in one
+    rounding: ``f32(y_prev + sum)`` (used to form the rank-ordered sum).
+    """
+    x = bf16_to_f64(x_shard_bits)
+    w = bf16_to_f64(w_shard_bits)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x shard and weight shard K differ")
+    acc = x @ w.T
+    if bias_bits is not None and rank == 0:
+        acc = acc + bf16_to_f64(bias_bits)[None, :]
+    if y_prev is not None:
+        acc = acc + np.asarray(y_prev, dtype=np.float32).astype(np.float64)
+    return f32(acc)
+
+
+def rank_ordered_sum(partials) -> np.ndarray:
+    """``S = f32(f32(P_0 + P_1) + P_2 ...)``: the partials summed in rank order."""
+    s = np.asarray(partials[0], dtype=np.float32)
+    for p in partials[1:]:
+        s = f32(s.astype(np.float64) + np.asarray(p, dtype=np.float32).astype(np.float64))
+    return s
+
+
+def mlp_rank(x_bits, w_fc_shard_bits, w_proj_shard_bits, rank=0, y_prev=None):
+    """[nanotron] ``MLP.forward`` for one rank: ``c_fc`` (column) -> GELU -> ``c_proj`` partial.
+
+    GELU is elementwise, so each rank applies it to its own columns and feeds
+    ``c_proj`` with no exchange in between.  ``g_r`` is bf16 (the intermediate
+    activation dtype), then the row partial is float32.
+    """
+    n_r = w_fc_shard_bits.shape[0]
+    g = column_linear(x_bits, w_fc_shard_bits, None, [n_r], 1, 0, act=ACT_GELU, out_dtype=OUT_BF16)
+    return g, row_linear_partial(g, w_proj_shard_bits, None, rank=rank, y_prev=y_prev)
+
+
+# --------------------------------------------------------------------------------------
+# O5 - RMSNorm prologue  [palm] allgather_layernorm, transformer_layer_weight_gathered
+# --------------------------------------------------------------------------------------
+
+def rmsnorm(x_bits, scale_bits=None, eps=RMS_EPS):
+    """bf16 RMS-normalised rows, as the [palm] layer computes them before ``q_wi``.
+
+    Per row: mean of squares in (at least) float32 over the whole hidden
+    dimension (one device holds the full row, so the page's cross-shard mean is
+    the plain mean); ``r = f32(1 / sqrt(ms + eps))``; ``n = bf16(f32(x * r))``.
+    With a learned scale the page adds 1 to the bf16 scale first, so
+    ``t = bf16(f32(1 + s))`` and ``y = bf16(n * t)`` (the product of two bf16
+    values is exact in float32).  Without a scale (the prefill layer's local
+    norm) ``y = n``.  Returns ``(y_bits uint16 [M, K], r float32 [M])``.
+    """
+    x = bf16_to_f64(x_bits)
+    k = x.shape[1]
+    ms = np.sum(x * x, axis=1) / k
+    r = f32(1.0 / np.sqrt(ms + eps))
+    n = bf16_round(f32(x * r.astype(np.float64)[:, None]))
+    if scale_bits is None:
+        return n, r
+    t = bf16_round(f32(1.0 + bf16_to_f64(scale_bits)))
+    y = bf16_round(f32(bf16_to_f64(n) * bf16_to_f64(t)[None, :]))
+    return y, r
+
+
+def rmsnorm_column_linear(x_bits, scale_bits, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size, rank,
+                          eps=RMS_EPS, out_dtype=OUT_BF16, layout=LAYOUT_LOCAL, n_logical=None):
+    """RMSNorm rows, then the rank's column linear on the bf16 normalised rows.
+
+    Returns ``(y, xnorm_bits)`` where ``y`` is as in ``column_linear``.
+    """
+    xn, _ = rmsnorm(x_bits, scale_bits, eps)
+    y = column_linear(xn, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size, rank,
+                      act=ACT_NONE, out_dtype=out_dtype, layout=layout, n_logical=n_logical)
+    return y, xn
+
+
+# --------------------------------------------------------------------------------------
+# O6/O7 - vocab-sharded LM head  [tt] LMHead1D; [palm] unembed_manual
+# --------------------------------------------------------------------------------------
+
+def lm_head_chunks(v_rows: int, max_rows_per_chunk: int):
+    """Chunk sizes and row offsets of a vocab shard of ``v_rows`` rows.
+
+    [tt] ``from_model_args``: ``num_splits = ceil(size / max)``, every split but
+    the last has ``min(size, max)`` rows and the last takes the remainder; the
+    splits are laid out back to back, so split ``c`` starts at ``c * max``.
+    """
+    if max_rows_per_chunk <= 0:
+        raise ValueError("max_rows_per_chunk must be positive")
+    n = -(-v_rows // max_rows_per_chunk)
+    sizes = [min(v_rows, max_rows_per_chunk)] * (n - 1)
+    sizes.append(v_rows - sum(sizes))
+    offs = [sum(sizes[:i]) for i in range(n)]
+    return sizes, offs
+
+
+def vocab_shard(vocab: int, tp_size: int, rank: int):
+    """``(rows, first_vocab_id)`` of the rank's vocab shard (O1 with one sub-parameter)."""
+    width, loff, _, _ = shard_widths([vocab], tp_size, rank)
+    return width[0], loff[0]
+
+
+def lm_head_logits(x_bits, w_shard_bits=None, w_fp8=None, w_scale=None, max_rows_per_chunk=None):
+    """float32 logits of one vocab shard, chunk by chunk, concatenated.
+
+    [tt] ``LMHead1D.forward``: one linear per weight split, outputs trimmed to
+    their logical widths and concatenated along the vocab dimension; each device
+    ends with the complete logits of its vocab shard (no partial sums).
+    [palm] ``unembed_manual`` computes logits in float32.
+
+    bf16 weight: ``logits[b,v] = f32(sum_k x[b,k] W[v,k])``.
+    E4M3 weight with per-row, per-128-K block scales (reading of the page's
+    8-bit block weight format):
+    ``logits[b,v] = f32(sum_blk s[v,blk] * sum_{k in blk} x[b,k] dec(q[v,k]))``.
+    """
+    x = bf16_to_f64(x_bits)
+    if w_shard_bits is not None:
+        w = bf16_to_f64(w_shard_bits)
+        v_rows = w.shape[0]
+
+        def chunk(lo, hi):
+            return x @ w[lo:hi].T
+    else:
+        q = e4m3_to_f64(w_fp8)
+        s = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+        v_rows, k = q.shape
+        if k % FP8_BLOCK:
+            raise ValueError("fp8 K must be a multiple of 128")
+        nb = k // FP8_BLOCK
+
+        def chunk(lo, hi):
+            part = np.zeros((x.shape[0], hi - lo))
+            for blk in range(nb):
+                ks = slice(blk * FP8_BLOCK, (blk + 1) * FP8_BLOCK)
+                part += (x[:, ks] @ q[lo:hi, ks].T) * s[lo:hi, blk][None, :]
+            return part
+    c = v_rows if max_rows_per_chunk is None else max_rows_per_chunk
+    sizes, offs = lm_head_chunks(v_rows, c)
+    outs = [chunk(o, o + n) for n, o in zip(sizes, offs)]
+    return f32(np.concatenate(outs, axis=1))
+
+
+def shard_argmax(logits32: np.ndarray):
+    """Per row, the lowest local index attaining the maximum logit, and that maximum.
+
+    [tt] leaves the argmax over the gathered shards to the caller; each shard's
+    candidate is its own maximum.  Reading: ties go to the lowest index; NaN
+    entries are ignored.  Returns ``(idx int32 [B], max float32 [B])``.
+    """
+    l = np.asarray(logits32, dtype=np.float32)
+    clean = np.where(np.isnan(l), -np.inf, l)
+    idx = np.argmax(clean, axis=1).astype(np.int32)  # numpy returns the first maximum
+    return idx, clean[np.arange(l.shape[0]), idx].astype(np.float32)
+
+
+def global_argmax(per_rank):
+    """Combine per-rank ``(idx, max, vocab_offset)`` triples: largest max, ties to the lowest rank."""
+    best_v = None
+    best_i = None
+    for idx, mx, off in per_rank:
+        g = idx.astype(np.int64) + off
+        if best_v is None:
+            best_v, best_i = mx.copy(), g.copy()
+        else:
+            better = mx > best_v
+            best_v = np.where(better, mx, best_v)
+            best_i = np.where(better, g, best_i)
+    return best_i, best_v
