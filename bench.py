@@ -1,0 +1,334 @@
+"""Benchmark of one tensor-parallel rank's transformer linear layers on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  1. GPT-2-small MLP shard, tp=2: ranks 0 and 1 in turn, c_fc + GELU then the c_proj
+     partial (rank 1 accumulates onto rank 0's partial: the rank-ordered sum);
+  2. fused-QKV GQA column shard (sizes 4096/1024/1024, tp=8 rank 0, bias);
+  3. Llama-8B MLP shard, tp=8: c_fc + GELU, c_proj float32 partial;
+  4. RMSNorm (scale + 1, eps 1e-6) into a column shard [3072, 8192];
+  5. vocab-sharded decode LM head (vocab 128256, tp=8 rank 0, 4 chunks of 4008 rows,
+     argmax), bf16 weights and E4M3 weights with 128-wide block scales.
+Every part is bracketed with HIP events on the stream its kernels run on. The headline
+value is the shard-GEMM throughput: the algorithmic GEMM flops of parts 1-4 (2 M N K per
+product; normalisation and activation work not counted) over those parts' time. The LM
+head is reported as achieved HBM bandwidth over the bytes it must move (the weight shard
+once, its scales, x and the logits). Weight copies of the LM head rotate so that every
+timed call streams from HBM (the 256 MB last-level cache cannot hold the rotation).
+
+Prints one JSON line. Inputs are seeded synthetic tensors of the workloads' shapes; they
+are on the device before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "shard GEMM TFLOP/s (% MFMA peak); LM-head decode GB/s (% HBM peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
+    ap.add_argument("--parts", default="1,2,3,4,5", help="comma list of workload parts to run")
+    return ap.parse_args()
+
+
+class Workloads:
+    """Device-resident inputs, weights and outputs of the five parts."""
+
+    def __init__(self, parts, dev):
+        import torch
+
+        import synth
+        import tensor_transformer_linear_amd as tt
+
+        self.tt, self.torch, self.parts = tt, torch, parts
+        W = synth.WORKLOADS
+
+        def d16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.flops = {}
+        if 1 in parts:
+            c = W[1]
+            inp = synth.workload_inputs(1)
+            self.c1 = c
+            self.x1 = d16(inp["x"])
+            self.wfc1, self.wpj1 = [], []
+            for r in range(c["tp"]):
+                w, lo, _, tot = tt.tp_shard_widths([c["inter"]], c["tp"], r)
+                self.wfc1.append(d16(inp["w_fc"][lo[0]:lo[0] + w[0]]))
+                self.wpj1.append(d16(np.ascontiguousarray(inp["w_proj"][:, lo[0]:lo[0] + w[0]])))
+            M = self.x1.shape[0]
+            self.g1 = [torch.empty((M, self.wfc1[r].shape[0]), dtype=torch.bfloat16, device=dev) for r in range(2)]
+            self.s1 = torch.empty((M, c["hidden"]), dtype=torch.float32, device=dev)
+            self.flops[1] = sum(2 * M * self.wfc1[r].shape[0] * c["hidden"] * 2 for r in range(c["tp"]))
+        if 2 in parts:
+            c = W[2]
+            inp = synth.workload_inputs(2)
+            self.c2 = c
+            width, lo, _, tot = tt.tp_shard_widths(list(c["sizes"]), c["tp"], c["rank"])
+            rows = np.concatenate([np.arange(o, o + w) for w, o in zip(width, lo)])
+            self.x2, self.w2, self.b2 = d16(inp["x"]), d16(inp["w"][rows]), d16(inp["bias"][rows])
+            self.y2 = torch.empty((self.x2.shape[0], tot), dtype=torch.bfloat16, device=dev)
+            self.flops[2] = 2 * self.x2.shape[0] * tot * c["hidden"]
+        if 3 in parts:
+            c = W[3]
+            inp = synth.workload_inputs(3)
+            self.c3 = c
+            self.x3, self.wfc3, self.wpj3 = d16(inp["x"]), d16(inp["w_fc"]), d16(inp["w_proj"])
+            M, n_r = self.x3.shape[0], self.wfc3.shape[0]
+            self.g3 = torch.empty((M, n_r), dtype=torch.bfloat16, device=dev)
+            self.p3 = torch.empty((M, c["hidden"]), dtype=torch.float32, device=dev)
+            self.flops[3] = 2 * M * n_r * c["hidden"] * 2
+        if 4 in parts:
+            c = W[4]
+            inp = synth.workload_inputs(4)
+            self.c4 = c
+            self.x4, self.s4, self.w4 = d16(inp["x"]), d16(inp["scale"]), d16(inp["w"])
+            M, n_r = self.x4.shape[0], self.w4.shape[0]
+            self.y4 = torch.empty((M, n_r), dtype=torch.bfloat16, device=dev)
+            self.ws4 = torch.empty(tt.tp_rmsnorm_workspace_bytes(M, c["hidden"]), dtype=torch.uint8, device=dev)
+            self.flops[4] = 2 * M * n_r * c["hidden"]
+        if 5 in parts:
+            c = W[5]
+            inp = synth.workload_inputs(5)
+            self.c5 = c
+            self.x5 = d16(inp["x"])
+            w = d16(inp["w"])
+            q = torch.from_numpy(inp["w_fp8"]).to(dev)
+            sc = torch.from_numpy(inp["w_scale"]).to(dev)
+            # rotation: >= 512 MB of weight copies per dtype, beyond the 256 MB last-level cache
+            n16 = max(2, -(-(512 << 20) // (w.numel() * 2)))
+            n8 = max(2, -(-(512 << 20) // (q.numel() + sc.numel() * 4)))
+            self.w5 = [w] + [w.clone() for _ in range(n16 - 1)]
+            self.q5 = [(q, sc)] + [(q.clone(), sc.clone()) for _ in range(n8 - 1)]
+            B, V_r = self.x5.shape[0], w.shape[0]
+            self.lg5 = torch.empty((B, V_r), dtype=torch.float32, device=dev)
+            self.am5 = torch.empty((B,), dtype=torch.int32, device=dev)
+            self.mx5 = torch.empty((B,), dtype=torch.float32, device=dev)
+            self.ws5 = tt.lm_head_workspace(B, c["vocab"], c["tp"], c["rank"], c["chunk"], dev)
+            K = c["hidden"]
+            self.bytes5 = {
+                "bf16": V_r * K * 2 + B * K * 2 + B * V_r * 4,
+                "fp8": V_r * K + V_r * (K // 128) * 4 + B * K * 2 + B * V_r * 4,
+            }
+            self.rot = 0
+
+    # --- the parts of one step -------------------------------------------------------------
+    def part1(self):
+        tt, c = self.tt, self.c1
+        for r in range(c["tp"]):
+            tt.tp_column_linear(self.x1, self.wfc1[r], None, [c["inter"]], c["tp"], r, act=tt.TP_ACT_GELU_ERF,
+                                y=self.g1[r])
+            tt.tp_row_linear_partial(self.g1[r], c["inter"], self.wpj1[r], None, c["tp"], r, y_partial=self.s1,
+                                     accumulate=int(r > 0))
+
+    def part2(self):
+        tt, c = self.tt, self.c2
+        tt.tp_column_linear(self.x2, self.w2, self.b2, list(c["sizes"]), c["tp"], c["rank"], y=self.y2)
+
+    def part3a(self):
+        tt, c = self.tt, self.c3
+        tt.tp_column_linear(self.x3, self.wfc3, None, [c["inter"]], c["tp"], c["rank"], act=tt.TP_ACT_GELU_ERF,
+                            y=self.g3)
+
+    def part3b(self):
+        tt, c = self.tt, self.c3
+        tt.tp_row_linear_partial(self.g3, c["inter"], self.wpj3, None, c["tp"], c["rank"], y_partial=self.p3)
+
+    def part4(self):
+        tt, c = self.tt, self.c4
+        tt.rmsnorm_column_linear(self.x4, self.s4, c["eps"], self.w4, None, [c["out_logical"]], c["tp"], c["rank"],
+                                 y=self.y4, workspace=self.ws4)
+
+    def part5(self, fp8):
+        tt, c = self.tt, self.c5
+        if fp8:
+            q, sc = self.q5[self.rot % len(self.q5)]
+            tt.lm_head_shard_argmax(self.x5, c["vocab"], c["tp"], c["rank"], c["chunk"], q, tt.TP_DTYPE_FP8_E4M3, sc,
+                                    logits=self.lg5, argmax_local=self.am5, max_logit=self.mx5, workspace=self.ws5)
+        else:
+            w = self.w5[self.rot % len(self.w5)]
+            tt.lm_head_shard_argmax(self.x5, c["vocab"], c["tp"], c["rank"], c["chunk"], w, logits=self.lg5,
+                                    argmax_local=self.am5, max_logit=self.mx5, workspace=self.ws5)
+
+    def segments(self):
+        s = []
+        if 1 in self.parts:
+            s.append(("gpt2_mlp_tp2_both_ranks", self.part1))
+        if 2 in self.parts:
+            s.append(("qkv_gqa_column", self.part2))
+        if 3 in self.parts:
+            s.append(("llama8b_c_fc_gelu", self.part3a))
+            s.append(("llama8b_c_proj_partial", self.part3b))
+        if 4 in self.parts:
+            s.append(("rmsnorm_column", self.part4))
+        if 5 in self.parts:
+            s.append(("lm_head_bf16", lambda: self.part5(False)))
+            s.append(("lm_head_fp8", lambda: self.part5(True)))
+        return s
+
+
+def cpu_baseline(budget_s: float):
+    """The oracle, as it stands, on row blocks of the RMSNorm -> column workload until the
+    time budget is spent; returns TFLOP/s of the GEMM flops it covered."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    c = synth.WORKLOADS[4]
+    rows_per_block = 256
+    inp = synth.workload_inputs(4, rows=rows_per_block * 64)
+    x, s, w = inp["x"], inp["scale"], inp["w"]
+    done = 0
+    t0 = time.perf_counter()
+    while done + rows_per_block <= x.shape[0]:
+        oracle.rmsnorm_column_linear(x[done:done + rows_per_block], s, w, None, [c["out_logical"]], c["tp"],
+                                     c["rank"])
+        done += rows_per_block
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.0 * done * w.shape[0] * c["hidden"]
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"RMSNorm -> column shard [3072, 8192] on the first {done} of 32768 rows "
+                  f"({dt:.1f} s, numpy float64, {os.cpu_count()} host cpus, {platform.processor() or platform.machine()})",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build emulates tensor-parallel ranks shard by shard on a "
+              f"single device and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import tensor_transformer_linear_amd as tt
+
+    tt.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    parts = {int(p) for p in args.parts.split(",") if p}
+    t_setup = time.perf_counter()
+    wl = Workloads(parts, dev)
+    torch.cuda.synchronize()
+    print(f"bench: inputs ready in {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+
+    segs = wl.segments()
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for i, (_, fn) in enumerate(segs):
+            if evs is not None:
+                evs[i][0].record(stream)
+            fn()
+            if evs is not None:
+                evs[i][1].record(stream)
+        if 5 in parts:
+            wl.rot += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in segs]
+              for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(events[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per_seg = {name: [events[k][i][0].elapsed_time(events[k][i][1]) for k in range(args.steps)]
+               for i, (name, _) in enumerate(segs)}
+    avg = {n: float(np.mean(v)) for n, v in per_seg.items()}
+    med = {n: float(np.median(v)) for n, v in per_seg.items()}
+    print("bench: per-part mean ms " + json.dumps({n: round(v, 4) for n, v in avg.items()}), file=sys.stderr,
+          flush=True)
+
+    gemm_names = {1: ["gpt2_mlp_tp2_both_ranks"], 2: ["qkv_gqa_column"],
+                  3: ["llama8b_c_fc_gelu", "llama8b_c_proj_partial"], 4: ["rmsnorm_column"]}
+    per_config = []
+    gemm_flops = gemm_ms = 0.0
+    for cfg in (1, 2, 3, 4):
+        if cfg not in parts:
+            continue
+        ms = sum(avg[n] for n in gemm_names[cfg])
+        tf = wl.flops[cfg] / (ms * 1e-3) / 1e12
+        gemm_flops += wl.flops[cfg]
+        gemm_ms += ms
+        per_config.append({"workload": cfg, "parts": gemm_names[cfg], "mean_us": round(ms * 1e3, 2),
+                           "median_us": round(sum(med[n] for n in gemm_names[cfg]) * 1e3, 2),
+                           "gflop": round(wl.flops[cfg] / 1e9, 3), "tflops": round(tf, 1),
+                           "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        if cfg == 3:
+            for n, fl in (("llama8b_c_fc_gelu", wl.flops[3] / 2), ("llama8b_c_proj_partial", wl.flops[3] / 2)):
+                per_config[-1][n + "_tflops"] = round(fl / (avg[n] * 1e-3) / 1e12, 1)
+    lm = {}
+    if 5 in parts:
+        for dt in ("bf16", "fp8"):
+            ms = avg[f"lm_head_{dt}"]
+            gbs = wl.bytes5[dt] / (ms * 1e-3) / 1e9
+            lm[dt] = {"mean_us": round(ms * 1e3, 2), "median_us": round(med[f"lm_head_{dt}"] * 1e3, 2),
+                      "bytes": wl.bytes5[dt], "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+            per_config.append({"workload": 5, "weights": dt, **lm[dt]})
+
+    value = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+    # dominant kernel launch: the largest single-part time among the GEMM parts
+    roofline = None
+    if gemm_ms > 0:
+        dom = max((n for c in gemm_names if c in parts for n in gemm_names[c]), key=lambda n: avg[n])
+        dom_flops = {"gpt2_mlp_tp2_both_ranks": wl.flops.get(1), "qkv_gqa_column": wl.flops.get(2),
+                     "llama8b_c_fc_gelu": wl.flops.get(3, 0) / 2, "llama8b_c_proj_partial": wl.flops.get(3, 0) / 2,
+                     "rmsnorm_column": wl.flops.get(4)}[dom]
+        ach = dom_flops / (avg[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                    "flops_per_launch": dom_flops, "mean_launch_us": round(avg[dom] * 1e3, 2)}
+    out = {
+        "metric": METRIC, "value": round(value, 2) if value else None, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations and N(0,0.02) random-init weights of the workloads' shapes",
+        "config": {"workload": "one pass of: gpt2-small MLP tp2 (both ranks), fused-QKV GQA column tp8 r0, "
+                               "llama-8B MLP tp8, RMSNorm->column [32768x8192]x[3072], decode LM head vocab 128256 "
+                               "tp8 r0 (bf16 and e4m3 weights)",
+                   "gemm_flops_per_step": gemm_flops, "gemm_ms_per_step": round(gemm_ms, 4),
+                   "parts": sorted(parts)},
+        "roofline": roofline,
+        "lm_head": lm or None,
+        "per_config": per_config,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * tpshard.h - C ABI of one tensor-parallel rank's share of a transformer block's
+ * linear layers, native to AMD Instinct MI355X (gfx950).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensors are row-major with the last dimension contiguous. "Device" pointers
+ *    are HIP device memory of the current device; "host" pointers are ordinary
+ *    CPU memory read before the call returns.
+ *  - bf16 tensors hold bfloat16 bit patterns (uint16); fp8 tensors hold OCP
+ *    E4M3FN bytes; f32 tensors hold IEEE float32.
+ *  - Device tensor pointers must be 16-byte aligned and every row length (K, and
+ *    the leading dimensions of outputs) must keep rows 16-byte aligned unless an
+ *    entry point says otherwise.
+ *  - Weights are [out_features, in_features] (the input dimension contiguous):
+ *    the linear computes y = x W^T (+ b).
+ *  - The caller allocates and owns every buffer, including workspaces. The
+ *    library allocates no memory and never synchronises: work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the null stream) and the call returns.
+ *  - Every argument check runs on the host before any HIP call. A failed check
+ *    returns a non-zero tp_status and enqueues nothing; tp_last_error() then
+ *    returns a message for the calling thread. A launch failure reported by the
+ *    HIP runtime returns TP_ERR_HIP.
+ *  - Ranks are arguments, not processes: one GPU computes any rank's share.
+ *
+ * Sources (web pages on tensor-parallel linear layers):
+ *  [nanotron]  nanotron rules page "Tensor-Parallel Component Patterns",
+ *              sections "Attention Module" and "MLP Module".
+ *  [deepspeed] DeepSpeed module_inject/layers.py, class SubParamLinearLayer
+ *              (docstring, __init__, forward).
+ *  [palm]      google-research scaling_transformer_inference_efficiency
+ *              layers/two_d_parallel_xmap.py: allgather_layernorm,
+ *              unembed_manual, transformer_layer_weight_gathered.
+ *  [tt]        Tenstorrent models/common/modules/lm_head/lm_head_1d.py:
+ *              module docstring, LMHead1DConfig, LMHead1D.forward,
+ *              LMHead1D.from_model_args.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point below is exported from libtpshard.so; nothing else is. */
+#if defined(__GNUC__) || defined(__clang__)
+#define TP_API __attribute__((visibility("default")))
+#else
+#define TP_API
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1, /* null pointer, tp_size < 1, rank outside [0, tp_size), non-positive size */
+  TP_ERR_SHAPE = 2,       /* sizes that do not fit together (sub-param < tp_size, bias length, chunking, workspace) */
+  TP_ERR_UNSUPPORTED = 3, /* alignment, K not a multiple of 8 (128 for fp8), unknown dtype/act/layout code */
+  TP_ERR_HIP = 4          /* the HIP runtime reported an error for a launch */
+} tp_status;
+
+typedef enum { TP_DTYPE_BF16 = 0, TP_DTYPE_F32 = 1, TP_DTYPE_FP8_E4M3 = 2 } tp_dtype;
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_ERF = 1 } tp_act;
+typedef enum { TP_LAYOUT_LOCAL = 0, TP_LAYOUT_LOGICAL = 1 } tp_layout;
+
+/* Largest number of sub-parameters one column-parallel weight may hold. */
+#define TP_MAX_SUBPARAMS 16
+
+/*
+ * tp_shard_widths - the rows of each sub-parameter that rank `rank` owns.
+ *
+ * [deepspeed] SubParamLinearLayer: a weight whose output dimension holds several
+ * logical sub-parameters (fused q/k/v with unequal GQA widths, chunked MLP) is
+ * partitioned sub-parameter by sub-parameter, and the per-rank widths are
+ * resolved once per model. [nanotron]: local sizes are `n // tp_size`.
+ * Where tp_size does not divide a size, the split is balanced and the
+ * remainder goes to the lowest ranks: w_s(r) = S_s / tp + (r < S_s % tp).
+ *
+ * subparam_sizes  host, n_sub logical sizes S_0..S_{n-1} (each >= tp_size)
+ * width           host out, n_sub: rows of each sub-parameter owned by `rank`
+ * logical_off     host out, n_sub: first logical row owned in each sub-parameter
+ * local_off       host out, n_sub: first row of each piece inside the rank's shard
+ * shard_total     host out, 1: rows of the rank's materialised shard
+ * The shard is the concatenation, in sub-parameter order, of the logical rows
+ * [logical_off[s], logical_off[s] + width[s]). Pure host arithmetic; any output
+ * pointer may be NULL. Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE.
+ */
+TP_API int tp_shard_widths(const int64_t* subparam_sizes, int n_sub, int tp_size, int rank,
+                    int64_t* width, int64_t* logical_off, int64_t* local_off, int64_t* shard_total);
+
+/*
+ * tp_column_linear - one rank's column-parallel linear with sub-parameter sharding.
+ *
+ * [deepspeed] SubParamLinearLayer.forward: the replicated input times the
+ * transposed shard weight, plus the shard bias. [nanotron] MLP: c_fc keeps
+ * intermediate // tp output columns per rank, then F.gelu.
+ *
+ * x           device bf16 [M, K]
+ * w_shard     device bf16 [N_r, K], N_r = shard total of (subparam_sizes, tp_size, rank):
+ *             the rank's rows of every sub-parameter, concatenated in sub-parameter order
+ * bias_shard  device bf16 [N_r] (the same row map) or NULL
+ * act         TP_ACT_NONE or TP_ACT_GELU_ERF (exact erf GELU of the float32 accumulator)
+ * y           device, y_dtype TP_DTYPE_BF16 or TP_DTYPE_F32:
+ *             TP_LAYOUT_LOCAL:   [M, ldy], ldy >= N_r; local column j is written at j
+ *             TP_LAYOUT_LOGICAL: [M, ldy], ldy >= sum(subparam_sizes); local column j of
+ *             sub-parameter s is written at its logical column
+ *             logical_off[s] + (j - local_off[s]); other columns are not touched
+ * Each output is rounded once: y = round(act(f32 sum_k x w + b)).
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED (K % 8, ldy % 8 for bf16
+ * or % 4 for f32, misalignment), TP_ERR_HIP.
+ */
+TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                     const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y,
+                     int y_dtype, int layout, int64_t ldy, void* stream);
+
+/*
+ * tp_row_linear_partial - one rank's row-parallel partial sum, before any reduction.
+ *
+ * [nanotron] TensorParallelRowLinear (the MLP's c_proj, the attention's output
+ * projection): each rank holds a slice of the input features and the matching
+ * weight columns; its product is the rank's float32 partial of the full output,
+ * which the pages then reduce across ranks with a collective.
+ *
+ * x_shard    device bf16 [M, K_r], K_r = the rank's width of K_logical (tp_shard_widths)
+ * w_shard    device bf16 [N, K_r]
+ * bias       device bf16 [N] or NULL; added by rank 0 only, so the ranks' partials sum
+ *            to the unsharded output
+ * y_partial  device f32 [M, N]; accumulate = 0 stores the partial, accumulate = 1 adds it
+ *            to the values already there with one float32 rounding (a rank-ordered sum
+ *            when the ranks run in order)
+ * Errors: as tp_column_linear (N % 4 for the f32 rows).
+ */
+TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
+                          const void* bias, int tp_size, int rank, float* y_partial, int accumulate,
+                          void* stream);
+
+/*
+ * tp_rmsnorm_workspace_bytes - device workspace rmsnorm_column_linear needs for M rows of K.
+ */
+TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * rmsnorm_column_linear - RMSNorm of each input row, then the rank's column linear on it.
+ *
+ * [palm] allgather_layernorm: float32 statistics, r = rsqrt(mean(x^2) + eps),
+ * n = bf16(x * r); with a learned scale the page first adds 1 to the bf16 scale
+ * (the T5X option that centres the learned scale at zero), so t = bf16(1 + s) and y = bf16(n * t).
+ * transformer_layer_weight_gathered normalises without a scale (scale = NULL).
+ * One device holds whole rows, so the page's mean across shards is the mean of
+ * the row.
+ *
+ * x          device bf16 [M, K]
+ * scale      device bf16 [K] or NULL
+ * eps        added to the mean square (the pages use 1e-6)
+ * xnorm_out  device bf16 [M, K] receiving y, or NULL
+ * w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, y, y_dtype, layout, ldy:
+ *            as tp_column_linear, with y's input rows being the normalised rows
+ * workspace  device, at least tp_rmsnorm_workspace_bytes(M, K) bytes, 256-byte aligned;
+ *            contents need no initialisation and are scratch between calls
+ * Errors: as tp_column_linear, TP_ERR_SHAPE for a short workspace.
+ */
+TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
+                          const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                          int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * tp_lm_head_workspace_bytes - device workspace lm_head_shard_argmax needs.
+ */
+TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk);
+
+/*
+ * lm_head_shard_argmax - a vocab shard's float32 logits and per-row argmax (decode).
+ *
+ * [tt] LMHead1D: the output projection of each device's vocab shard is split
+ * into chunks of at most max_rows_per_chunk rows (every chunk but the last has
+ * that many rows, the last the remainder), one linear runs per chunk and the
+ * outputs are concatenated, so each device holds the complete logits of its own
+ * vocab rows (column-parallel, no partial sums); the argmax across devices is
+ * left to the caller. [palm] unembed_manual computes logits in float32.
+ *
+ * x                 device bf16 [B, K]
+ * vocab, tp_size, rank  the shard is tp_shard_widths({vocab}, ...): V_r rows starting
+ *                   at vocab id logical_off (returned indices are local to the shard)
+ * w_shard           device [V_r, K], w_dtype TP_DTYPE_BF16 or TP_DTYPE_FP8_E4M3
+ * w_block_scale     fp8 only: device f32 [V_r, K / 128], the scale of each row's
+ *                   128-wide K block (value = scale * E4M3 value); NULL for bf16
+ * logits            device f32 [B, V_r]; chunk c's rows land at columns c*max_rows_per_chunk...
+ * argmax_local      device int32 [B]: lowest local index of the row's largest logit
+ * max_logit         device f32 [B] or NULL: that largest logit
+ * workspace         device, tp_lm_head_workspace_bytes(...) bytes, 256-byte aligned. Zero
+ *                   it once before the first call; every call leaves it zeroed again.
+ *                   Calls that overlap in time must not share a workspace.
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE (chunk size <= 0, workspace short),
+ * TP_ERR_UNSUPPORTED (K % 8, fp8 with K % 128, dtype), TP_ERR_HIP.
+ */
+TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                         int64_t max_rows_per_chunk, const void* w_shard, int w_dtype, const float* w_block_scale,
+                         float* logits, int32_t* argmax_local, float* max_logit, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * tp_last_error - message of the last non-OK status returned on the calling thread
+ * ("" if none). The pointer stays valid until the thread's next call into the library.
+ */
+TP_API const char* tp_last_error(void);
+
+/*
+ * tp_version - library version string (static storage).
+ */
+TP_API const char* tp_version(void);
+
+/*
+ * Tuning and testing hooks (calling thread only).
+ * tp_debug_set_gemm_tile   forces the GEMM tile configuration of later calls on this
+ *                          thread: -1 restores the automatic choice, 0..6 select
+ *                          256x256, 256x128, 128x128, 128x256, 256x224, 128x64, 64x64
+ *                          (output rows x columns per workgroup). TP_ERR_INVALID_ARG
+ *                          for other values.
+ * tp_debug_gemm_pick_tile  the automatic choice for an M x N x K problem (-1 if invalid).
+ */
+TP_API int tp_debug_set_gemm_tile(int tile);
+TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -41,9 +41,10 @@ def rng(cfg_id: int, tensor_id: int) -> np.random.Generator:
 def _f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 bit patterns (nearest, ties to even)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    # no uint32 overflow: the largest non-NaN pattern is 0xFF800000 (-inf)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
@@ -110,19 +111,25 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     return (code | (neg.astype(np.uint8) << 7)).astype(np.uint8)
 
 
-def quantize_e4m3_blocks(w_bits: np.ndarray):
+def quantize_e4m3_blocks(w_bits: np.ndarray, chunk_rows: int = 2048):
     """Per-row, per-128-K-block E4M3 storage of a bf16 weight ``[rows, K]``.
 
-    Returns ``(codes uint8 [rows, K], scales float32 [rows, K // 128])``.
+    Returns ``(codes uint8 [rows, K], scales float32 [rows, K // 128])``.  Rows are
+    processed in blocks to bound the temporaries; each row's result is independent.
     """
     rows, k = w_bits.shape
     if k % FP8_BLOCK:
         raise ValueError(f"K={k} must be a multiple of {FP8_BLOCK}")
-    w = (w_bits.astype(np.uint32) << 16).view(np.float32).reshape(rows, k // FP8_BLOCK, FP8_BLOCK)
-    amax = np.abs(w).max(axis=2)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = e4m3_encode((w / scale[:, :, None]).astype(np.float32))
-    return q.reshape(rows, k), scale
+    q = np.empty((rows, k), dtype=np.uint8)
+    scale = np.empty((rows, k // FP8_BLOCK), dtype=np.float32)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        w = (w_bits[r0:r1].astype(np.uint32) << 16).view(np.float32).reshape(r1 - r0, k // FP8_BLOCK, FP8_BLOCK)
+        amax = np.abs(w).max(axis=2)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q[r0:r1] = e4m3_encode((w / s[:, :, None]).astype(np.float32)).reshape(r1 - r0, k)
+        scale[r0:r1] = s
+    return q, scale
 
 
 # --- The five workloads, as shapes and distributions ---------------------------------

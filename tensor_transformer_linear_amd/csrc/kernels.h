@@ -1,0 +1,74 @@
+// Host-side launch interfaces of the gfx950 kernels (internal to libtpshard).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tpshard.h"
+
+namespace tpk {
+
+// Output stage of the NT GEMM: y = round(act(acc + bias)), stored at a remapped column.
+struct GemmEpilogue {
+  const uint16_t* bias;  // bf16 [N] or nullptr
+  void* C;               // bf16 or f32 output
+  int64_t ldc;           // elements between output rows
+  int act;               // TP_ACT_*
+  int out_f32;           // 0: bf16 output, 1: f32 output
+  int accumulate;        // f32 only: C += result (one rounding)
+  int n_seg;             // column segments; 0 = output column is the local column
+  int seg_end[TP_MAX_SUBPARAMS];    // exclusive local end column of each segment
+  int seg_delta[TP_MAX_SUBPARAMS];  // output column minus local column inside the segment
+};
+
+// C[M,N] = A[M,K] * B[N,K]^T with both operands K-contiguous (weights as stored).
+struct GemmProblem {
+  const uint16_t* A;  // bf16 [M, lda]
+  int64_t lda;
+  const uint16_t* B;  // bf16 [N, ldb]
+  int64_t ldb;
+  int M, N, K;
+  // Optional RMSNorm applied to A while it is staged: a' = bf16(bf16(a * row_r[m]) * col_t[k]),
+  // or bf16(a * row_r[m]) when col_t is null.
+  const float* row_r;     // f32 [M] or nullptr (no normalisation)
+  const uint16_t* col_t;  // bf16 [K] or nullptr
+  GemmEpilogue ep;
+};
+
+// Tile configurations the launcher can pick (see gemm.hip for their shapes).
+enum GemmTile : int {
+  TILE_AUTO = -1,
+  TILE_256x256 = 0,
+  TILE_256x128 = 1,
+  TILE_128x128 = 2,
+  TILE_128x256 = 3,
+  TILE_256x224 = 4,
+  TILE_128x64 = 5,
+  TILE_64x64 = 6,
+  TILE_COUNT = 7
+};
+
+hipError_t launch_gemm(const GemmProblem& p, int tile, hipStream_t stream);
+int gemm_pick_tile(int M, int N, int K);
+
+// RMSNorm statistics: r[m] = rsqrt(mean_k x^2 + eps) for every row, t[k] = bf16(1 + s[k]),
+// and, when xnorm is non-null, the normalised bf16 rows.
+hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, const uint16_t* scale, float eps, float* r,
+                               uint16_t* t, uint16_t* xnorm, hipStream_t stream);
+
+struct LmHeadProblem {
+  const uint16_t* x;     // bf16 [B, K]
+  const void* w;         // bf16 or e4m3 [V, K]
+  const float* wscale;   // f32 [V, K/128] (fp8) or nullptr
+  int w_fp8;
+  int B, K, V;
+  int chunk;             // rows per chunk (last chunk takes the remainder)
+  float* logits;         // f32 [B, V]
+  int32_t* argmax;       // int32 [B]
+  float* maxval;         // f32 [B] or nullptr
+  void* workspace;
+};
+size_t lm_head_workspace_bytes(int B, int V, int chunk);
+hipError_t launch_lm_head(const LmHeadProblem& p, hipStream_t stream);
+
+}  // namespace tpk

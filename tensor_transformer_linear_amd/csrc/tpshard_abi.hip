@@ -1,0 +1,313 @@
+// C ABI of libtpshard: argument checks, shard arithmetic and kernel dispatch.
+//
+// Every check runs on the host before any HIP call; a failed check sets the
+// calling thread's message and returns a status without touching the GPU.
+#include <limits.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_tile_override = tpk::TILE_AUTO;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// The balanced split with the remainder on the lowest ranks.
+int64_t width_of(int64_t size, int tp, int r) { return size / tp + (r < size % tp ? 1 : 0); }
+
+struct Shard {
+  int n_sub;
+  int64_t width[TP_MAX_SUBPARAMS], logical_off[TP_MAX_SUBPARAMS], local_off[TP_MAX_SUBPARAMS];
+  int64_t total, logical_total;
+};
+
+int resolve_shard(const int64_t* sizes, int n_sub, int tp_size, int rank, Shard* s) {
+  if (sizes == nullptr) return fail(TP_ERR_INVALID_ARG, "subparam_sizes is NULL");
+  if (n_sub < 1 || n_sub > TP_MAX_SUBPARAMS)
+    return fail(TP_ERR_INVALID_ARG, "n_sub = %d outside [1, %d]", n_sub, TP_MAX_SUBPARAMS);
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  s->n_sub = n_sub;
+  int64_t base = 0, local = 0;
+  for (int i = 0; i < n_sub; ++i) {
+    const int64_t S = sizes[i];
+    if (S <= 0) return fail(TP_ERR_INVALID_ARG, "sub-parameter %d has size %lld", i, (long long)S);
+    if (S < tp_size)
+      return fail(TP_ERR_SHAPE, "sub-parameter %d has size %lld, smaller than tp_size %d", i, (long long)S, tp_size);
+    if (S > (int64_t)INT_MAX || base > (int64_t)INT_MAX - S)
+      return fail(TP_ERR_UNSUPPORTED, "logical output width exceeds %d", INT_MAX);
+    int64_t before = 0;
+    for (int q = 0; q < rank; ++q) before += width_of(S, tp_size, q);
+    s->width[i] = width_of(S, tp_size, rank);
+    s->logical_off[i] = base + before;
+    s->local_off[i] = local;
+    local += s->width[i];
+    base += S;
+  }
+  s->total = local;
+  s->logical_total = base;
+  return TP_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Checks shared by the column-parallel entry points; fills the GEMM problem.
+int prepare_column(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                   const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y, int y_dtype,
+                   int layout, int64_t ldy, tpk::GemmProblem* p) {
+  Shard sh;
+  int st = resolve_shard(subparam_sizes, n_sub, tp_size, rank, &sh);
+  if (st != TP_OK) return st;
+  if (M < 0) return fail(TP_ERR_INVALID_ARG, "M = %lld must be >= 0", (long long)M);
+  if (w_shard == nullptr) return fail(TP_ERR_INVALID_ARG, "w_shard must be non-NULL");
+  if (M > 0 && (x == nullptr || y == nullptr)) return fail(TP_ERR_INVALID_ARG, "x and y must be non-NULL");
+  if (K <= 0) return fail(TP_ERR_INVALID_ARG, "K = %lld must be positive", (long long)K);
+  if (M > INT_MAX || K > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and K must fit in 31 bits");
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU_ERF) return fail(TP_ERR_UNSUPPORTED, "unknown act %d", act);
+  if (y_dtype != TP_DTYPE_BF16 && y_dtype != TP_DTYPE_F32)
+    return fail(TP_ERR_UNSUPPORTED, "y_dtype %d: output must be bf16 or f32", y_dtype);
+  if (layout != TP_LAYOUT_LOCAL && layout != TP_LAYOUT_LOGICAL) return fail(TP_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  const int64_t need = layout == TP_LAYOUT_LOCAL ? sh.total : sh.logical_total;
+  if (ldy < need)
+    return fail(TP_ERR_SHAPE, "ldy = %lld is smaller than the %s output width %lld", (long long)ldy,
+                layout == TP_LAYOUT_LOCAL ? "local" : "logical", (long long)need);
+  const int vec = y_dtype == TP_DTYPE_BF16 ? 8 : 4;
+  if (ldy % vec) return fail(TP_ERR_UNSUPPORTED, "ldy = %lld must be a multiple of %d", (long long)ldy, vec);
+  if (!aligned(x, 16) || !aligned(w_shard, 16) || !aligned(y, 16))
+    return fail(TP_ERR_UNSUPPORTED, "x, w_shard and y must be 16-byte aligned");
+  if (bias_shard != nullptr && !aligned(bias_shard, 2)) return fail(TP_ERR_UNSUPPORTED, "bias_shard misaligned");
+
+  memset(p, 0, sizeof(*p));
+  p->A = static_cast<const uint16_t*>(x);
+  p->lda = K;
+  p->B = static_cast<const uint16_t*>(w_shard);
+  p->ldb = K;
+  p->M = (int)M;
+  p->N = (int)sh.total;
+  p->K = (int)K;
+  p->ep.bias = static_cast<const uint16_t*>(bias_shard);
+  p->ep.C = y;
+  p->ep.ldc = ldy;
+  p->ep.act = act;
+  p->ep.out_f32 = y_dtype == TP_DTYPE_F32;
+  p->ep.accumulate = 0;
+  p->ep.n_seg = 0;
+  if (layout == TP_LAYOUT_LOGICAL) {
+    p->ep.n_seg = sh.n_sub;
+    for (int i = 0; i < sh.n_sub; ++i) {
+      p->ep.seg_end[i] = (int)(sh.local_off[i] + sh.width[i]);
+      p->ep.seg_delta[i] = (int)(sh.logical_off[i] - sh.local_off[i]);
+    }
+  }
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+TP_API const char* tp_last_error(void) { return g_err; }
+
+TP_API const char* tp_version(void) { return "tpshard 0.1 gfx950"; }
+
+TP_API int tp_shard_widths(const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int64_t* width,
+                    int64_t* logical_off, int64_t* local_off, int64_t* shard_total) {
+  Shard sh;
+  int st = resolve_shard(subparam_sizes, n_sub, tp_size, rank, &sh);
+  if (st != TP_OK) return st;
+  for (int i = 0; i < n_sub; ++i) {
+    if (width) width[i] = sh.width[i];
+    if (logical_off) logical_off[i] = sh.logical_off[i];
+    if (local_off) local_off[i] = sh.local_off[i];
+  }
+  if (shard_total) *shard_total = sh.total;
+  return ok();
+}
+
+TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                     const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y, int y_dtype,
+                     int layout, int64_t ldy, void* stream) {
+  tpk::GemmProblem p;
+  int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, act, y, y_dtype, layout,
+                          ldy, &p);
+  if (st != TP_OK) return st;
+  if (M == 0) return ok();
+  return hip_status(tpk::launch_gemm(p, g_tile_override, as_stream(stream)), "tp_column_linear launch");
+}
+
+TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
+                          const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (w_shard == nullptr || (M > 0 && (x_shard == nullptr || y_partial == nullptr)))
+    return fail(TP_ERR_INVALID_ARG, "x_shard, w_shard and y_partial must be non-NULL");
+  if (M < 0 || N <= 0 || K_logical <= 0)
+    return fail(TP_ERR_INVALID_ARG, "M = %lld, N = %lld, K_logical = %lld: need M >= 0, N > 0, K_logical > 0",
+                (long long)M, (long long)N, (long long)K_logical);
+  if (K_logical < tp_size)
+    return fail(TP_ERR_SHAPE, "K_logical = %lld is smaller than tp_size %d", (long long)K_logical, tp_size);
+  if (M > INT_MAX || N > INT_MAX || K_logical > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  const int64_t K_r = width_of(K_logical, tp_size, rank);
+  if (K_r % 8) return fail(TP_ERR_UNSUPPORTED, "the rank's input width %lld must be a multiple of 8", (long long)K_r);
+  if (N % 4) return fail(TP_ERR_UNSUPPORTED, "N = %lld must be a multiple of 4", (long long)N);
+  if (!aligned(x_shard, 16) || !aligned(w_shard, 16) || !aligned(y_partial, 16))
+    return fail(TP_ERR_UNSUPPORTED, "x_shard, w_shard and y_partial must be 16-byte aligned");
+  if (bias != nullptr && !aligned(bias, 2)) return fail(TP_ERR_UNSUPPORTED, "bias misaligned");
+  if (M == 0) return ok();
+
+  tpk::GemmProblem p;
+  memset(&p, 0, sizeof(p));
+  p.A = static_cast<const uint16_t*>(x_shard);
+  p.lda = K_r;
+  p.B = static_cast<const uint16_t*>(w_shard);
+  p.ldb = K_r;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K_r;
+  p.ep.bias = rank == 0 ? static_cast<const uint16_t*>(bias) : nullptr;
+  p.ep.C = y_partial;
+  p.ep.ldc = N;
+  p.ep.act = TP_ACT_NONE;
+  p.ep.out_f32 = 1;
+  p.ep.accumulate = accumulate;
+  return hip_status(tpk::launch_gemm(p, g_tile_override, as_stream(stream)), "tp_row_linear_partial launch");
+}
+
+TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return align_up((size_t)M * sizeof(float), 256) + align_up((size_t)K * sizeof(uint16_t), 256);
+}
+
+TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
+                          const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                          int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  tpk::GemmProblem p;
+  int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, TP_ACT_NONE, y, y_dtype,
+                          layout, ldy, &p);
+  if (st != TP_OK) return st;
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(TP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (scale != nullptr && !aligned(scale, 16)) return fail(TP_ERR_UNSUPPORTED, "scale must be 16-byte aligned");
+  if (xnorm_out != nullptr && !aligned(xnorm_out, 16))
+    return fail(TP_ERR_UNSUPPORTED, "xnorm_out must be 16-byte aligned");
+  if (workspace == nullptr && M > 0) return fail(TP_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t need = tp_rmsnorm_workspace_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  if (M == 0) return ok();
+
+  float* r = static_cast<float*>(workspace);
+  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + align_up((size_t)M * 4, 256));
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpk::launch_rmsnorm_rows(static_cast<const uint16_t*>(x), (int)M, (int)K,
+                                          static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr,
+                                          static_cast<uint16_t*>(xnorm_out), s);
+  if (e != hipSuccess) return hip_status(e, "rmsnorm statistics launch");
+  if (xnorm_out != nullptr) {
+    // The normalised rows are materialised anyway: the GEMM reads them as a plain A.
+    p.A = static_cast<const uint16_t*>(xnorm_out);
+  } else {
+    p.row_r = r;
+    p.col_t = scale ? t : nullptr;
+  }
+  return hip_status(tpk::launch_gemm(p, g_tile_override, s), "rmsnorm_column_linear GEMM launch");
+}
+
+TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk) {
+  if (B < 1 || vocab < 1 || tp_size < 1 || rank < 0 || rank >= tp_size || max_rows_per_chunk < 1 || vocab < tp_size ||
+      vocab > INT_MAX)
+    return 0;
+  const int64_t V_r = width_of(vocab, tp_size, rank);
+  const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
+  return tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
+}
+
+TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                         int64_t max_rows_per_chunk, const void* w_shard, int w_dtype, const float* w_block_scale,
+                         float* logits, int32_t* argmax_local, float* max_logit, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (x == nullptr || w_shard == nullptr || logits == nullptr || argmax_local == nullptr || workspace == nullptr)
+    return fail(TP_ERR_INVALID_ARG, "x, w_shard, logits, argmax_local and workspace must be non-NULL");
+  if (B < 1 || K < 1 || vocab < 1)
+    return fail(TP_ERR_INVALID_ARG, "B = %lld, K = %lld, vocab = %lld must be positive", (long long)B, (long long)K,
+                (long long)vocab);
+  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
+  if (B > INT_MAX || K > INT_MAX || vocab > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (max_rows_per_chunk < 1)
+    return fail(TP_ERR_SHAPE, "max_rows_per_chunk = %lld must be positive", (long long)max_rows_per_chunk);
+  if (w_dtype != TP_DTYPE_BF16 && w_dtype != TP_DTYPE_FP8_E4M3)
+    return fail(TP_ERR_UNSUPPORTED, "w_dtype %d: the weight must be bf16 or fp8 e4m3", w_dtype);
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (w_dtype == TP_DTYPE_FP8_E4M3) {
+    if (K % 128) return fail(TP_ERR_UNSUPPORTED, "fp8 weights need K (%lld) a multiple of 128", (long long)K);
+    if (w_block_scale == nullptr) return fail(TP_ERR_INVALID_ARG, "fp8 weights need w_block_scale");
+    if (!aligned(w_block_scale, 4)) return fail(TP_ERR_UNSUPPORTED, "w_block_scale misaligned");
+  }
+  if (!aligned(x, 16) || !aligned(w_shard, 16) || !aligned(logits, 4) || !aligned(argmax_local, 4) ||
+      (max_logit != nullptr && !aligned(max_logit, 4)))
+    return fail(TP_ERR_UNSUPPORTED, "x and w_shard must be 16-byte aligned, outputs 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const int64_t V_r = width_of(vocab, tp_size, rank);
+  const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
+  const size_t need = tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
+  if (workspace_bytes < need) return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  tpk::LmHeadProblem p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = w_shard;
+  p.wscale = w_dtype == TP_DTYPE_FP8_E4M3 ? w_block_scale : nullptr;
+  p.w_fp8 = w_dtype == TP_DTYPE_FP8_E4M3;
+  p.B = (int)B;
+  p.K = (int)K;
+  p.V = (int)V_r;
+  p.chunk = (int)chunk;
+  p.logits = logits;
+  p.argmax = argmax_local;
+  p.maxval = max_logit;
+  p.workspace = workspace;
+  return hip_status(tpk::launch_lm_head(p, as_stream(stream)), "lm_head_shard_argmax launch");
+}
+
+TP_API int tp_debug_set_gemm_tile(int tile) {
+  if (tile < tpk::TILE_AUTO || tile >= tpk::TILE_COUNT) return fail(TP_ERR_INVALID_ARG, "unknown tile %d", tile);
+  g_tile_override = tile;
+  return ok();
+}
+
+TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return -1;
+  return tpk::gemm_pick_tile((int)M, (int)N, (int)K);
+}
+
+}  // extern "C"

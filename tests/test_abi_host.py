@@ -1,0 +1,196 @@
+"""Host-side tests of libtpshard: exports, shard arithmetic and argument checks (no GPU work).
+
+Every call here either is pure host arithmetic or fails a check that the
+library runs before any HIP call, so the suite runs without a GPU. Device
+pointers are stand-in addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+
+tt = pytest.importorskip("tensor_transformer_linear_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+if not os.path.exists(tt.LIB_PATH):
+    pytest.skip("libtpshard.so is not built", allow_module_level=True)
+
+L = tt.lib()
+A = ctypes.c_void_p(0x10000)       # 16-byte aligned stand-in device address
+A2 = ctypes.c_void_p(0x20000)
+A3 = ctypes.c_void_p(0x30000)
+WS = ctypes.c_void_p(0x40000)      # 256-byte aligned
+MIS = ctypes.c_void_p(0x10002)     # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"^TP_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_match_header():
+    declared = declared_functions()
+    assert {"tp_shard_widths", "tp_column_linear", "tp_row_linear_partial", "rmsnorm_column_linear",
+            "lm_head_shard_argmax"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", tt.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == declared
+    assert declared == set(tt.SIGNATURES)
+
+
+def test_version():
+    assert "gfx950" in tt.version()
+
+
+@pytest.mark.parametrize("sizes,tp", [([4096, 1024, 1024], 8), ([3072], 2), ([14336], 8), ([24576], 8),
+                                      ([128256], 8), ([7, 5, 5], 3), ([100, 30, 17], 7), ([9], 9), ([1], 1)])
+def test_shard_widths_bit_exact_vs_oracle(sizes, tp):
+    for r in range(tp):
+        assert tt.tp_shard_widths(sizes, tp, r) == oracle.shard_widths(sizes, tp, r)
+
+
+def test_shard_widths_configs():
+    assert tt.tp_shard_widths([4096, 1024, 1024], 8, 0) == ([512, 128, 128], [0, 4096, 5120], [0, 512, 640], 768)
+    assert tt.tp_shard_widths([128256], 8, 3)[1:] == ([3 * 16032], [0], 16032)
+
+
+@pytest.mark.parametrize("sizes,tp,rank,status", [
+    ([3], 4, 0, tt.TP_ERR_SHAPE), ([8], 0, 0, tt.TP_ERR_INVALID_ARG), ([8], 2, 2, tt.TP_ERR_INVALID_ARG),
+    ([8], 2, -1, tt.TP_ERR_INVALID_ARG), ([0], 1, 0, tt.TP_ERR_INVALID_ARG), ([-4], 1, 0, tt.TP_ERR_INVALID_ARG),
+    ([8] * 17, 1, 0, tt.TP_ERR_INVALID_ARG),
+])
+def test_shard_widths_errors(sizes, tp, rank, status):
+    with pytest.raises(tt.TpError) as e:
+        tt.tp_shard_widths(sizes, tp, rank)
+    assert e.value.status == status and e.value.message
+
+
+def _sizes(vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def col(**kw):
+    a = dict(x=A, M=64, K=128, w=A2, b=None, sizes=[64, 32, 32], tp=2, rank=0, act=0, y=A3, yd=0, layout=0, ldy=64)
+    a.update(kw)
+    s = a["sizes"]
+    return L.tp_column_linear(a["x"], a["M"], a["K"], a["w"], a["b"], _sizes(s) if s is not None else None,
+                              len(s) if s is not None else 1, a["tp"], a["rank"], a["act"], a["y"], a["yd"],
+                              a["layout"], a["ldy"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(w=None), tt.TP_ERR_INVALID_ARG), (dict(y=None), tt.TP_ERR_INVALID_ARG),
+    (dict(sizes=None), tt.TP_ERR_INVALID_ARG), (dict(M=-1), tt.TP_ERR_INVALID_ARG), (dict(K=0), tt.TP_ERR_INVALID_ARG),
+    (dict(K=12), tt.TP_ERR_UNSUPPORTED), (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(rank=2), tt.TP_ERR_INVALID_ARG),
+    (dict(sizes=[64, 1, 32]), tt.TP_ERR_SHAPE), (dict(act=7), tt.TP_ERR_UNSUPPORTED), (dict(yd=2), tt.TP_ERR_UNSUPPORTED),
+    (dict(layout=5), tt.TP_ERR_UNSUPPORTED), (dict(ldy=56), tt.TP_ERR_SHAPE),
+    (dict(layout=1, ldy=64), tt.TP_ERR_SHAPE),                 # logical width is 128
+    (dict(ldy=68), tt.TP_ERR_UNSUPPORTED),                      # bf16 rows must stay 16-byte aligned
+    (dict(x=MIS), tt.TP_ERR_UNSUPPORTED), (dict(y=MIS), tt.TP_ERR_UNSUPPORTED),
+    (dict(b=ctypes.c_void_p(0x10001)), tt.TP_ERR_UNSUPPORTED), (dict(M=2 ** 31), tt.TP_ERR_UNSUPPORTED),
+])
+def test_column_linear_rejects(kw, status):
+    assert col(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_column_linear_empty_input_is_a_no_op():
+    assert col(M=0) == tt.TP_OK
+    assert L.tp_last_error().decode() == ""
+
+
+def row(**kw):
+    a = dict(x=A, M=16, Kl=256, N=64, w=A2, b=None, tp=2, rank=1, y=A3, acc=0)
+    a.update(kw)
+    return L.tp_row_linear_partial(a["x"], a["M"], a["Kl"], a["N"], a["w"], a["b"], a["tp"], a["rank"], a["y"],
+                                   a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(y=None), tt.TP_ERR_INVALID_ARG), (dict(N=0), tt.TP_ERR_INVALID_ARG),
+    (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(rank=5), tt.TP_ERR_INVALID_ARG), (dict(acc=2), tt.TP_ERR_INVALID_ARG),
+    (dict(Kl=1), tt.TP_ERR_SHAPE), (dict(Kl=250), tt.TP_ERR_UNSUPPORTED), (dict(N=66), tt.TP_ERR_UNSUPPORTED),
+    (dict(w=MIS), tt.TP_ERR_UNSUPPORTED),
+])
+def test_row_partial_rejects(kw, status):
+    assert row(**kw) == status
+
+
+def test_row_partial_empty():
+    assert row(M=0) == tt.TP_OK
+
+
+def rms(**kw):
+    a = dict(x=A, M=8, K=128, s=None, eps=1e-6, xn=None, w=A2, sizes=[64], tp=1, rank=0, y=A3, ldy=64, ws=WS,
+             wsb=1 << 20)
+    a.update(kw)
+    return L.rmsnorm_column_linear(a["x"], a["M"], a["K"], a["s"], a["eps"], a["xn"], a["w"], None,
+                                   _sizes(a["sizes"]), len(a["sizes"]), a["tp"], a["rank"], a["y"], 0, 0, a["ldy"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), tt.TP_ERR_INVALID_ARG), (dict(wsb=100), tt.TP_ERR_SHAPE), (dict(eps=-1.0), tt.TP_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), tt.TP_ERR_INVALID_ARG), (dict(eps=float("inf")), tt.TP_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x40010)), tt.TP_ERR_UNSUPPORTED), (dict(s=MIS), tt.TP_ERR_UNSUPPORTED),
+    (dict(xn=MIS), tt.TP_ERR_UNSUPPORTED), (dict(K=100), tt.TP_ERR_UNSUPPORTED), (dict(x=None), tt.TP_ERR_INVALID_ARG),
+])
+def test_rmsnorm_rejects(kw, status):
+    assert rms(**kw) == status
+
+
+def test_rmsnorm_workspace_size():
+    assert tt.tp_rmsnorm_workspace_bytes(32768, 8192) == 32768 * 4 + 8192 * 2
+    assert tt.tp_rmsnorm_workspace_bytes(3, 8) == 256 + 256
+
+
+def lm(**kw):
+    a = dict(x=A, B=32, K=256, vocab=1024, tp=8, rank=0, chunk=64, w=A2, wd=0, sc=None, lg=A3, am=A3, mx=None,
+             ws=WS, wsb=1 << 20)
+    a.update(kw)
+    return L.lm_head_shard_argmax(a["x"], a["B"], a["K"], a["vocab"], a["tp"], a["rank"], a["chunk"], a["w"],
+                                  a["wd"], a["sc"], a["lg"], a["am"], a["mx"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(ws=None), tt.TP_ERR_INVALID_ARG), (dict(B=0), tt.TP_ERR_INVALID_ARG),
+    (dict(vocab=4), tt.TP_ERR_SHAPE), (dict(chunk=0), tt.TP_ERR_SHAPE), (dict(wd=1), tt.TP_ERR_UNSUPPORTED),
+    (dict(K=100), tt.TP_ERR_UNSUPPORTED), (dict(wd=2, K=192), tt.TP_ERR_UNSUPPORTED),
+    (dict(wd=2, sc=None), tt.TP_ERR_INVALID_ARG), (dict(wsb=16), tt.TP_ERR_SHAPE), (dict(rank=8), tt.TP_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x40040)), tt.TP_ERR_UNSUPPORTED), (dict(w=MIS), tt.TP_ERR_UNSUPPORTED),
+])
+def test_lm_head_rejects(kw, status):
+    assert lm(**kw) == status
+
+
+def test_lm_head_workspace_query():
+    n = tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0, 4008)
+    assert n > 0
+    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 8, 4008) == 0
+    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0, 0) == 0
+
+
+def test_debug_tile_hook():
+    with pytest.raises(tt.TpError):
+        tt.set_gemm_tile(99)
+    tt.set_gemm_tile(3)
+    tt.set_gemm_tile(-1)
+    assert tt.gemm_pick_tile(0, 1, 1) == -1
+    assert tt.gemm_pick_tile(32768, 3072, 8192) in tt.GEMM_TILES
+
+
+def test_product_path_does_not_use_the_oracle_or_generator():
+    pkg_dir = os.path.dirname(tt.__file__)
+    for root, _, files in os.walk(pkg_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                for word in ("import oracle", "from oracle", "import synth", "from synth", "tp_oracle"):
+                    assert word not in text, (f, word)
