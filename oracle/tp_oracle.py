@@ -7,7 +7,7 @@ shares no code, header, table or constant generator with it.
 Everything here is the plain definition of what the hot path computes, written
 out in numpy float64 from exactly widened bf16 / E4M3 inputs, then rounded once
 where the method rounds.  A library primitive (numpy's float64 matmul, scipy's
-double-precision ``erf``) serves as a step; there is no blocking, fusion or
+double-precision ``erfc``) serves as a step; there is no blocking, fusion or
 reordering beyond the definitions.  Sources (web pages):
 
   [nanotron]  nanotron rules page "Tensor-Parallel Component Patterns",
@@ -35,7 +35,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
-from scipy.special import erf as _erf
+from scipy.special import erfc as _erfc
 
 RMS_EPS = 1e-6
 FP8_BLOCK = 128
@@ -179,13 +179,15 @@ def take_row_shard(w_logical: np.ndarray, tp_size: int, rank: int) -> np.ndarray
 # --------------------------------------------------------------------------------------
 
 def gelu_erf(a32: np.ndarray) -> np.ndarray:
-    """Exact (erf) GELU of float32 values, evaluated in double: 0.5 a (1 + erf(a / sqrt 2)).
+    """Exact (erf) GELU of float32 values in double: a * Phi(a) = 0.5 a (1 + erf(a / sqrt 2)).
 
     [nanotron] applies ``F.gelu`` between ``c_fc`` and ``c_proj``; ``F.gelu``'s
     default and [cerebras] ``Transformer(activation='gelu')`` are the erf form.
+    ``1 + erf(z)`` is evaluated as ``erfc(-z)`` (the same function): the sum
+    cancels in float64 for a < -5, where erfc keeps full relative accuracy.
     """
     a = np.asarray(a32, dtype=np.float64)
-    return 0.5 * a * (1.0 + _erf(a / math.sqrt(2.0)))
+    return 0.5 * a * _erfc(-a / math.sqrt(2.0))
 
 
 def column_linear(x_bits, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size, rank,
