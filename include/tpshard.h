@@ -9,9 +9,9 @@
  *    CPU memory read before the call returns.
  *  - bf16 tensors hold bfloat16 bit patterns (uint16); fp8 tensors hold OCP
  *    E4M3FN bytes; f32 tensors hold IEEE float32.
- *  - Device tensor pointers must be 16-byte aligned and every row length (K, and
- *    the leading dimensions of outputs) must keep rows 16-byte aligned unless an
- *    entry point says otherwise.
+ *  - Device tensor pointers must be 16-byte aligned and the input rows (K) must
+ *    keep 16-byte alignment (K a multiple of 8 bf16 values) unless an entry point
+ *    says otherwise; output leading dimensions are free.
  *  - Weights are [out_features, in_features] (the input dimension contiguous):
  *    the linear computes y = x W^T (+ b).
  *  - The caller allocates and owns every buffer, including workspaces. The
@@ -107,8 +107,9 @@ TP_API int tp_shard_widths(const int64_t* subparam_sizes, int n_sub, int tp_size
  *             sub-parameter s is written at its logical column
  *             logical_off[s] + (j - local_off[s]); other columns are not touched
  * Each output is rounded once: y = round(act(f32 sum_k x w + b)).
- * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED (K % 8, ldy % 8 for bf16
- * or % 4 for f32, misalignment), TP_ERR_HIP.
+ * M = 0 is an empty input: nothing is enqueued and x, y may be NULL.
+ * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED (K % 8, misalignment),
+ * TP_ERR_HIP.
  */
 TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
                      const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y,
@@ -129,7 +130,7 @@ TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_s
  * y_partial  device f32 [M, N]; accumulate = 0 stores the partial, accumulate = 1 adds it
  *            to the values already there with one float32 rounding (a rank-ordered sum
  *            when the ranks run in order)
- * Errors: as tp_column_linear (N % 4 for the f32 rows).
+ * Errors: as tp_column_linear; the rank's input width K_r must be a multiple of 8.
  */
 TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
                           const void* bias, int tp_size, int rank, float* y_partial, int accumulate,

@@ -23,8 +23,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
-// Exact (erf) GELU in float32: 0.5 a (1 + erf(a / sqrt 2)).
-__device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f)); }
+// Exact (erf) GELU in float32: 0.5 a (1 + erf(a / sqrt 2)), evaluated as 0.5 a erfc(-a / sqrt 2)
+// (the same function) so that large negative inputs keep their relative accuracy instead of
+// cancelling in 1 + erf.
+__device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * erfcf(-a * 0.70710678118654752f); }
 
 // Number of XCDs of an MI355X; consecutive workgroup ids are dispatched round-robin over them.
 constexpr int kNumXcd = 8;

@@ -98,8 +98,6 @@ int prepare_column(const void* x, int64_t M, int64_t K, const void* w_shard, con
   if (ldy < need)
     return fail(TP_ERR_SHAPE, "ldy = %lld is smaller than the %s output width %lld", (long long)ldy,
                 layout == TP_LAYOUT_LOCAL ? "local" : "logical", (long long)need);
-  const int vec = y_dtype == TP_DTYPE_BF16 ? 8 : 4;
-  if (ldy % vec) return fail(TP_ERR_UNSUPPORTED, "ldy = %lld must be a multiple of %d", (long long)ldy, vec);
   if (!aligned(x, 16) || !aligned(w_shard, 16) || !aligned(y, 16))
     return fail(TP_ERR_UNSUPPORTED, "x, w_shard and y must be 16-byte aligned");
   if (bias_shard != nullptr && !aligned(bias_shard, 2)) return fail(TP_ERR_UNSUPPORTED, "bias_shard misaligned");
@@ -177,7 +175,6 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
   if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_INVALID_ARG, "accumulate must be 0 or 1");
   const int64_t K_r = width_of(K_logical, tp_size, rank);
   if (K_r % 8) return fail(TP_ERR_UNSUPPORTED, "the rank's input width %lld must be a multiple of 8", (long long)K_r);
-  if (N % 4) return fail(TP_ERR_UNSUPPORTED, "N = %lld must be a multiple of 4", (long long)N);
   if (!aligned(x_shard, 16) || !aligned(w_shard, 16) || !aligned(y_partial, 16))
     return fail(TP_ERR_UNSUPPORTED, "x_shard, w_shard and y_partial must be 16-byte aligned");
   if (bias != nullptr && !aligned(bias, 2)) return fail(TP_ERR_UNSUPPORTED, "bias misaligned");

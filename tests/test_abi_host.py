@@ -92,7 +92,6 @@ def col(**kw):
     (dict(sizes=[64, 1, 32]), tt.TP_ERR_SHAPE), (dict(act=7), tt.TP_ERR_UNSUPPORTED), (dict(yd=2), tt.TP_ERR_UNSUPPORTED),
     (dict(layout=5), tt.TP_ERR_UNSUPPORTED), (dict(ldy=56), tt.TP_ERR_SHAPE),
     (dict(layout=1, ldy=64), tt.TP_ERR_SHAPE),                 # logical width is 128
-    (dict(ldy=68), tt.TP_ERR_UNSUPPORTED),                      # bf16 rows must stay 16-byte aligned
     (dict(x=MIS), tt.TP_ERR_UNSUPPORTED), (dict(y=MIS), tt.TP_ERR_UNSUPPORTED),
     (dict(b=ctypes.c_void_p(0x10001)), tt.TP_ERR_UNSUPPORTED), (dict(M=2 ** 31), tt.TP_ERR_UNSUPPORTED),
 ])
@@ -116,7 +115,7 @@ def row(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(y=None), tt.TP_ERR_INVALID_ARG), (dict(N=0), tt.TP_ERR_INVALID_ARG),
     (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(rank=5), tt.TP_ERR_INVALID_ARG), (dict(acc=2), tt.TP_ERR_INVALID_ARG),
-    (dict(Kl=1), tt.TP_ERR_SHAPE), (dict(Kl=250), tt.TP_ERR_UNSUPPORTED), (dict(N=66), tt.TP_ERR_UNSUPPORTED),
+    (dict(Kl=1), tt.TP_ERR_SHAPE), (dict(Kl=250), tt.TP_ERR_UNSUPPORTED),
     (dict(w=MIS), tt.TP_ERR_UNSUPPORTED),
 ])
 def test_row_partial_rejects(kw, status):

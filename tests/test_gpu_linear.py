@@ -66,7 +66,9 @@ def test_column_linear_gaussian_gelu(tile):
             got = host_bits(y) if yd == tt.TP_DTYPE_BF16 else host_f32(y)
             ref = oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=act, out_dtype=yd)
             e = assert_close(got, ref, what=f"act={act} dtype={yd}")
-            assert e < 2e-3  # f32 accumulation vs exact: far inside the tolerance
+            # far inside the tolerance: f32 outputs differ by summation rounding only, bf16
+            # outputs by at most one bf16 ulp of the largest values
+            assert e < (1e-4 if yd == tt.TP_DTYPE_F32 else 1e-2)
 
 
 def test_gelu_every_finite_bf16():
