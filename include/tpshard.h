@@ -219,9 +219,14 @@ TP_API const char* tp_version(void);
  *                          256x256, 256x128, 128x128, 128x256, 256x224, 128x64, 64x64
  *                          (output rows x columns per workgroup). TP_ERR_INVALID_ARG
  *                          for other values.
+ * tp_debug_set_gemm_path   forces the GEMM main loop of later calls on this thread: -1
+ *                          automatic, 0 register-staged operands, 1 direct-to-LDS loads
+ *                          (needs K % 32 == 0 and no RMSNorm transform; a call that cannot
+ *                          use it returns TP_ERR_HIP).
  * tp_debug_gemm_pick_tile  the automatic choice for an M x N x K problem (-1 if invalid).
  */
 TP_API int tp_debug_set_gemm_tile(int tile);
+TP_API int tp_debug_set_gemm_path(int path);
 TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

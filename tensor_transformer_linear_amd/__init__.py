@@ -40,6 +40,7 @@ SIGNATURES = {
     "tp_last_error": (ctypes.c_char_p, []),
     "tp_version": (ctypes.c_char_p, []),
     "tp_debug_set_gemm_tile": (_int, [_int]),
+    "tp_debug_set_gemm_path": (_int, [_int]),
     "tp_debug_gemm_pick_tile": (_int, [_i64, _i64, _i64]),
 }
 
@@ -193,6 +194,14 @@ def lm_head_shard_argmax(x, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w
 def set_gemm_tile(tile: int) -> None:
     """Force a GEMM tile configuration on this thread (-1 = automatic); for tests and tuning."""
     _check(lib().tp_debug_set_gemm_tile(tile))
+
+
+def set_gemm_path(path: int) -> None:
+    """Force the GEMM main loop on this thread: -1 automatic, 0 register staging, 1 direct-to-LDS."""
+    _check(lib().tp_debug_set_gemm_path(path))
+
+
+GEMM_PATH_AUTO, GEMM_PATH_REGISTER, GEMM_PATH_DMA = -1, 0, 1
 
 
 def gemm_pick_tile(M: int, N: int, K: int) -> int:

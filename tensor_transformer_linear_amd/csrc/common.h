@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "tpshard.h"
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // one MFMA bf16 operand (8 K-values per lane)
@@ -27,6 +29,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // (the same function) so that large negative inputs keep their relative accuracy instead of
 // cancelling in 1 + erf.
 __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * erfcf(-a * 0.70710678118654752f); }
+
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>). Register arrays indexed
+// by these constants stay in registers whatever the unroller decides.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Number of XCDs of an MI355X; consecutive workgroup ids are dispatched round-robin over them.
 constexpr int kNumXcd = 8;

@@ -7,11 +7,11 @@
 //
 // Structure: one workgroup owns a BM x BN output tile and walks K in steps of
 // 64. Each step's A and B slabs go global -> registers -> LDS (two LDS stages:
-// the loads for step k+1 are in flight while step k's MFMAs run). Each wave owns
+// the loads of step k+1 are in flight while step k's MFMAs run). Each wave owns
 // a WM x WN sub-tile made of 32x32 blocks, computed with
 // v_mfma_f32_32x32x16_bf16 from 16-byte LDS reads. LDS rows are 128 bytes
-// (64 bf16 of K); the 16-byte chunk index is XORed with the row's low three
-// bits so that the eight rows one ds_read_b128 phase touches hit distinct banks.
+// (64 bf16 of K); the 16-byte chunk index is XORed with bits 1..3 of the row so
+// that the sixteen rows one ds_read_b128 phase touches hit distinct banks.
 // Optionally the A slab is RMS-normalised on its way into LDS.
 // The output stage adds the bias, applies GELU, rounds once and stores bf16
 // or f32 at the (possibly remapped) output column, or adds into f32.
@@ -25,7 +25,13 @@ namespace {
 constexpr int BK = 64;
 constexpr int ROW_BYTES = BK * 2;
 
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * ROW_BYTES + ((kc ^ (row & 7)) << 4); }
+// LDS byte offset of 16-byte chunk kc (0..7) of tile row `row`. The LDS serves a wave's
+// ds_read_b128 sixteen lanes at a time across 64 four-byte banks (256 bytes); the 16 lanes
+// read 16 consecutive rows at one logical chunk. Rows are 128 bytes, so row parity picks the
+// half of the 256-byte bank window and (row / 2) % 8 permutes the chunk within the half:
+// the 16 reads land on 16 distinct bank groups. The 8 lanes that write one row also cover 8
+// distinct chunks.
+__device__ __forceinline__ int lds_off(int row, int kc) { return row * ROW_BYTES + ((kc ^ ((row >> 1) & 7)) << 4); }
 
 // bf16(bf16(a * r) * t) (or bf16(a * r) without a scale) on eight packed values.
 __device__ __forceinline__ u32x4_t rms_apply(u32x4_t a, float r, u32x4_t t, bool has_t) {
@@ -39,6 +45,99 @@ __device__ __forceinline__ u32x4_t rms_apply(u32x4_t a, float r, u32x4_t t, bool
     o[i] = n;
   }
   return o;
+}
+
+// Output stage of a BM x BN tile, one 32-row band of every wave at a time. In a 32x32
+// accumulator block, lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of
+// its sixteen values v. Each wave parks its band (32 rows x WN columns) in LDS; the
+// workgroup then reads the staged band back four consecutive columns per thread and
+// finishes them: bias, GELU, one rounding, the column remap, and a coalesced store (or a
+// float32 add). `smem` must hold WAVES_M * 32 * (BN + 4) floats and be free.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN>
+__device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (&acc)[FM][FN], unsigned char* smem,
+                                                int m0, int n0, int wm, int wn, int lane, int tid) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  const int M = p.M, N = p.N;
+  constexpr int SROW = BN + 4;                       // staged row pitch in floats (bank offset)
+  constexpr int SROWS = WAVES_M * 32;                // staged rows per band
+  float* stage = reinterpret_cast<float*>(smem);
+  const GemmEpilogue& ep = p.ep;
+  constexpr int C4 = BN / 4;                         // four-column chunks per staged row
+  constexpr int CHUNKS = SROWS * C4;
+  static_assert(CHUNKS % NT == 0, "band chunks must divide evenly over the workgroup");
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<16>([&](auto v) {
+        constexpr int vv = v;
+        const int r = wm * 32 + (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+        stage[r * SROW + wn * WN + j * 32 + (lane & 31)] = acc[i][j][vv];
+      });
+    });
+    __syncthreads();
+    for (int q = 0; q < CHUNKS / NT; ++q) {
+      const int id = tid + q * NT;
+      const int sr = id / C4, c4 = id - sr * C4;
+      const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+      const int col = n0 + c4 * 4;
+      if (row < M && col < N) {
+        f32x4_t val = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4);
+        // output column of the chunk's first column, and whether all four share its segment
+        int d = 0, seg_end = N;
+        for (int sg = 0; sg < ep.n_seg; ++sg)
+          if (col < ep.seg_end[sg]) {
+            d = ep.seg_delta[sg];
+            seg_end = ep.seg_end[sg];
+            break;
+          }
+        const bool whole = col + 4 <= seg_end && col + 4 <= N;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (ep.bias != nullptr && col + e < N) val[e] += bf16_to_f32(ep.bias[col + e]);
+          if (ep.act == TP_ACT_GELU_ERF) val[e] = gelu_erf(val[e]);
+        }
+        const int64_t base = (int64_t)row * ep.ldc;
+        if (ep.out_f32) {
+          float* c = reinterpret_cast<float*>(ep.C) + base + col + d;
+          if (whole && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
+            f32x4_t* c4p = reinterpret_cast<f32x4_t*>(c);
+            if (ep.accumulate) val += *c4p;
+            *c4p = val;
+          } else {
+            for (int e = 0; e < 4 && col + e < N; ++e) {
+              int de = d;
+              for (int sg = 0; sg < ep.n_seg; ++sg)
+                if (col + e < ep.seg_end[sg]) {
+                  de = ep.seg_delta[sg];
+                  break;
+                }
+              float* ce = reinterpret_cast<float*>(ep.C) + base + col + e + de;
+              *ce = ep.accumulate ? *ce + val[e] : val[e];
+            }
+          }
+        } else {
+          uint16_t* c = reinterpret_cast<uint16_t*>(ep.C) + base + col + d;
+          if (whole && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
+            uint2 pk;
+            pk.x = pack_bf16x2(val[0], val[1]);
+            pk.y = pack_bf16x2(val[2], val[3]);
+            *reinterpret_cast<uint2*>(c) = pk;
+          } else {
+            for (int e = 0; e < 4 && col + e < N; ++e) {
+              int de = d;
+              for (int sg = 0; sg < ep.n_seg; ++sg)
+                if (col + e < ep.seg_end[sg]) {
+                  de = ep.seg_delta[sg];
+                  break;
+                }
+              reinterpret_cast<uint16_t*>(ep.C)[base + col + e + de] = f32_to_bf16(val[e]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  });
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool NORM>
@@ -69,9 +168,6 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
   const int M = p.M, N = p.N, K = p.K;
   const int kc = tid & 7;          // this thread's 16-byte chunk within a 64-wide K slab
   const int lrow = tid >> 3;       // first tile row this thread loads
-  const uint16_t* a_base = p.A + (int64_t)(m0 + lrow) * p.lda + kc * 8;
-  const uint16_t* b_base = p.B + (int64_t)(n0 + lrow) * p.ldb + kc * 8;
-  const int64_t a_step = (int64_t)ROWS_PER_PASS * p.lda, b_step = (int64_t)ROWS_PER_PASS * p.ldb;
 
   float rr[NORM ? CA : 1];
   const bool has_t = NORM && p.col_t != nullptr;
@@ -83,131 +179,247 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
     }
   }
 
-  u32x4_t ra[CA], rb[CB], rt;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
-    const bool kok = k0 + kc * 8 < K;
+  // Out-of-range rows and K chunks load from a clamped (valid) address and are zeroed when
+  // they are written to LDS.
+  bool a_ok[CA], b_ok[CB];
+  int64_t a_off[CA], b_off[CB];
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      bool ok = kok && (m0 + lrow + i * ROWS_PER_PASS < M);
-      ra[i] = ok ? *reinterpret_cast<const u32x4_t*>(a_base + i * a_step + k0) : zero;
-    }
+  for (int i = 0; i < CA; ++i) {
+    const int gm = m0 + lrow + i * ROWS_PER_PASS;
+    a_ok[i] = gm < M;
+    a_off[i] = (int64_t)(a_ok[i] ? gm : M - 1) * p.lda + kc * 8;
+  }
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      bool ok = kok && (n0 + lrow + i * ROWS_PER_PASS < N);
-      rb[i] = ok ? *reinterpret_cast<const u32x4_t*>(b_base + i * b_step + k0) : zero;
-    }
-    if (has_t) rt = kok ? *reinterpret_cast<const u32x4_t*>(p.col_t + k0 + kc * 8) : zero;
+  for (int i = 0; i < CB; ++i) {
+    const int gn = n0 + lrow + i * ROWS_PER_PASS;
+    b_ok[i] = gn < N;
+    b_off[i] = (int64_t)(b_ok[i] ? gn : N - 1) * p.ldb + kc * 8;
+  }
+  // One K step's operand pieces in registers.
+  struct Regs {
+    u32x4_t a[CA], b[CB], t;
   };
-  auto lstore = [&](int buf) {
+  // Issues the loads of step kt (clamped to the last step, so the call is unconditional and
+  // the compiler can count the loads in flight); nothing reads them until lstore.
+  const int nk = (K + BK - 1) / BK;
+  auto gload = [&](int kt, Regs& r) {
+    kt = kt < nk ? kt : nk - 1;
+    const int k0 = kt * BK;
+    const int kk0 = k0 + kc * 8 < K ? k0 : 0;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(p.A + a_off[i] + kk0);
+#pragma unroll
+    for (int i = 0; i < CB; ++i) r.b[i] = *reinterpret_cast<const u32x4_t*>(p.B + b_off[i] + kk0);
+    if (has_t) r.t = *reinterpret_cast<const u32x4_t*>(p.col_t + kk0 + kc * 8);
+  };
+  // Writes step kt's pieces into LDS stage `buf` (zeros outside the matrices).
+  auto lstore = [&](int buf, int kt, const Regs& r) {
+    const bool kok = kt * BK + kc * 8 < K;
     unsigned char* sa = smem + buf * STAGE;
     unsigned char* sb = sa + BM * ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      u32x4_t v = ra[i];
-      if constexpr (NORM) v = rms_apply(v, rr[i], rt, has_t);
+      u32x4_t v = (kok && a_ok[i]) ? r.a[i] : zero;
+      if constexpr (NORM) v = rms_apply(v, rr[i], r.t, has_t);
       *reinterpret_cast<u32x4_t*>(sa + lds_off(lrow + i * ROWS_PER_PASS, kc)) = v;
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<u32x4_t*>(sb + lds_off(lrow + i * ROWS_PER_PASS, kc)) = rb[i];
+      *reinterpret_cast<u32x4_t*>(sb + lds_off(lrow + i * ROWS_PER_PASS, kc)) = (kok && b_ok[i]) ? r.b[i] : zero;
   };
 
   f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<16>([&](auto v) { acc[i][j][decltype(v)::value] = 0.0f; });
+    });
+  });
 
   const int a_row0 = wm * WM + (lane & 31), b_row0 = wn * WN + (lane & 31);
   const int khalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) gload((kt + 1) * BK);
-    const unsigned char* sa = smem + (kt & 1) * STAGE;
+  auto compute = [&](int buf) {
+    const unsigned char* sa = smem + buf * STAGE;
     const unsigned char* sb = sa + BM * ROW_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    static_for<BK / 16>([&](auto kk) {
       bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
+      static_for<FM>([&](auto i) {
         af[i] = __builtin_bit_cast(bf16x8_t,
                                    *reinterpret_cast<const u32x4_t*>(sa + lds_off(a_row0 + i * 32, kk * 2 + khalf)));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
+      });
+      static_for<FN>([&](auto j) {
         bfr[j] = __builtin_bit_cast(bf16x8_t,
                                     *reinterpret_cast<const u32x4_t*>(sb + lds_off(b_row0 + j * 32, kk * 2 + khalf)));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) lstore((kt + 1) & 1);
+      });
+      static_for<FM>([&](auto i) {
+        static_for<FN>([&](auto j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        });
+      });
+    });
+  };
+
+  // Pipeline over K steps: one register set and two LDS stages. While step kt is
+  // multiplied out of LDS stage kt % 2, the loads of step kt + 1 are in flight; after the
+  // MFMAs they are written to the other stage. One barrier per step: the barrier closing
+  // step kt - 1 proves that every wave finished reading the stage step kt + 1 overwrites.
+  // Loads are unconditional (clamped to the last step) so the compiler keeps them in flight
+  // across the MFMAs.
+  Regs r0;
+  gload(0, r0);
+  lstore(0, 0, r0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    gload(kt + 1, r0);
+    compute(kt & 1);
+    lstore((kt + 1) & 1, kt + 1, r0);
     __syncthreads();
   }
 
-  // Output stage. In a 32x32 accumulator block, lane l holds column l % 32 and
-  // rows 8 * (v / 4) + 4 * (l / 32) + v % 4 for its sixteen values v.
-  const GemmEpilogue& ep = p.ep;
-  int ocol[FN];
-  float bias[FN];
-  bool cok[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    int c = n0 + wn * WN + j * 32 + (lane & 31);
-    cok[j] = c < N;
-    int d = 0;
-    for (int s = 0; s < ep.n_seg; ++s)
-      if (c < ep.seg_end[s]) {
-        d = ep.seg_delta[s];
-        break;
-      }
-    ocol[j] = c + d;
-    bias[j] = (ep.bias != nullptr && cok[j]) ? bf16_to_f32(ep.bias[c]) : 0.0f;
-  }
-  const int rbase = m0 + wm * WM + (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = rbase + i * 32 + (v >> 2) * 8 + (v & 3);
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if (!cok[j]) continue;
-        float val = acc[i][j][v] + bias[j];
-        if (ep.act == TP_ACT_GELU_ERF) val = gelu_erf(val);
-        const int64_t off = (int64_t)row * ep.ldc + ocol[j];
-        if (ep.out_f32) {
-          float* c = reinterpret_cast<float*>(ep.C) + off;
-          if (ep.accumulate) val = *c + val;
-          *c = val;
-        } else {
-          reinterpret_cast<uint16_t*>(ep.C)[off] = f32_to_bf16(val);
-        }
-      }
-    }
-  }
+  static_assert(WAVES_M * 32 * (BN + 4) * 4 <= 2 * STAGE, "band staging must fit in the pipeline's LDS");
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
-struct TileInfo {
-  int bm, bn, threads;
-};
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-hipError_t launch_tile(const GemmProblem& p, hipStream_t stream) {
+// Direct-to-LDS variant for K a multiple of 32 and no A transform. Each K step (32 wide)
+// of A and B is fetched with global_load_lds_dwordx4: every lane's 16 bytes go straight
+// into LDS (M0 base + 16 x lane), so no VGPRs hold operands in flight and the prefetch
+// depth is set by LDS: STAGES stages, STAGES - 1 of them loading while one is multiplied.
+// LDS rows are 64 bytes (32 bf16 of K); the 16-byte chunk index is XORed with bits 2..3
+// of the row, so the sixteen consecutive rows one ds_read_b128 phase reads fall on
+// sixteen distinct bank groups. A 1 KB DMA block is 16 rows; lane q of a block fetches the
+// global chunk that belongs at its LDS slot (row q / 4, physical chunk q % 4). Rows beyond
+// M or N read a clamped row: they only feed outputs that are never stored.
+constexpr int DBK = 32;
+constexpr int DROW = DBK * 2;  // 64-byte LDS rows
+
+__device__ __forceinline__ int dma_off(int row, int c) { return row * DROW + ((c ^ ((row >> 2) & 3)) << 4); }
+
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma_load16(const uint16_t* g, lds_byte* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+__global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
+                                                                            int group_m) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int NWAVE = NT / 64;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int NBLK_A = BM / 16, NBLK = (BM + BN) / 16;  // 1 KB DMA blocks per stage
+  constexpr int BLK_PER_WAVE = (NBLK + NWAVE - 1) / NWAVE;
+  // Every wave issues the same number of loads per stage (blocks past NBLK load a valid
+  // row into padding), so one vmcnt immediate fits all waves.
+  constexpr int STAGE = NWAVE * BLK_PER_WAVE * 1024;
+  static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be whole 32x32 blocks");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "tile rows must fill DMA blocks");
+  constexpr int EPI = WAVES_M * 32 * (BN + 4) * 4;
+  constexpr int SMEM = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = group_m * tiles_n;
+  const int grp = lid / per_group, first_m = grp * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int in = lid - grp * per_group;
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nk = K / DBK;
+
+  // Per DMA block this wave issues: the global source of this lane's 16 bytes.
+  const uint16_t* src[BLK_PER_WAVE];
+  int dst[BLK_PER_WAVE];
+#pragma unroll
+  for (int b = 0; b < BLK_PER_WAVE; ++b) {
+    const int blk = wave + b * NWAVE;
+    const int row = (blk < NBLK_A ? blk : blk - NBLK_A) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);  // logical chunk stored at this lane's slot
+    if (blk < NBLK_A) {
+      const int gm = min(m0 + row, M - 1);
+      src[b] = p.A + (int64_t)gm * p.lda + c * 8;
+    } else {
+      const int gn = blk < NBLK ? min(n0 + row, N - 1) : 0;
+      src[b] = p.B + (int64_t)gn * p.ldb + c * 8;
+    }
+    dst[b] = blk * 1024;
+  }
+  auto issue = [&](int kt) {
+    kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
+    lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + kt * DBK, base + dst[b]);
+  };
+
+  f32x16_t acc[FM][FN];
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) { static_for<16>([&](auto v) { acc[i][j][decltype(v)::value] = 0.0f; }); });
+  });
+  const int a_row0 = wm * WM + (lane & 31), b_row0 = wn * WN + (lane & 31);
+  const int khalf = lane >> 5;
+  auto compute = [&](int stage) {
+    const unsigned char* sa = smem + stage * STAGE;
+    const unsigned char* sb = sa + BM * DROW;
+    static_for<DBK / 16>([&](auto kk) {
+      bf16x8_t af[FM], bfr[FN];
+      static_for<FM>([&](auto i) {
+        af[i] = __builtin_bit_cast(bf16x8_t,
+                                   *reinterpret_cast<const u32x4_t*>(sa + dma_off(a_row0 + i * 32, kk * 2 + khalf)));
+      });
+      static_for<FN>([&](auto j) {
+        bfr[j] = __builtin_bit_cast(bf16x8_t,
+                                    *reinterpret_cast<const u32x4_t*>(sb + dma_off(b_row0 + j * 32, kk * 2 + khalf)));
+      });
+      static_for<FM>([&](auto i) {
+        static_for<FN>([&](auto j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        });
+      });
+    });
+  };
+
+  // Prologue: stages 0 .. STAGES-2 in flight. Step kt: wait until only the STAGES-2 newer
+  // stages' loads of this wave are outstanding, barrier (all waves' loads of stage kt have
+  // landed, and every wave finished step kt-1, whose buffer the next issue overwrites),
+  // issue step kt + STAGES - 1, multiply step kt.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // s_waitcnt with vmcnt = (STAGES - 2) * BLK_PER_WAVE, expcnt and lgkmcnt left open
+    // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+    constexpr int VM = (STAGES - 2) * BLK_PER_WAVE;
+    static_assert(VM < 64, "vmcnt immediate is six bits");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+    // Workgroup barrier without a memory fence: a fence would make the compiler drain every
+    // outstanding load (vmcnt 0) and serialise the stages. The wait above already covers
+    // this wave's loads of stage kt; the empty asm statements keep the compiler from moving
+    // LDS accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(kt + STAGES - 1);
+    compute(kt % STAGES);
+  }
+  __syncthreads();
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nb = tiles_m * tiles_n;
   const int group_m = tiles_m < 8 ? tiles_m : 8;
   dim3 grid(nb), block(WAVES_M * WAVES_N * 64);
-  if (p.row_r != nullptr)
+  const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
+  if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
+  if (dma_ok && path != GEMM_PATH_REGISTER)
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>), grid, block, 0, stream, p, tiles_m,
+                       tiles_n, group_m);
+  else if (p.row_r != nullptr)
     hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
                        group_m);
   else
@@ -231,16 +443,16 @@ int gemm_pick_tile(int M, int N, int K) {
   return TILE_64x64;
 }
 
-hipError_t launch_gemm(const GemmProblem& p, int tile, hipStream_t stream) {
+hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream) {
   if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.N, p.K);
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, 2, 2>(p, stream);
-    case TILE_256x128: return launch_tile<256, 128, 2, 2>(p, stream);
-    case TILE_128x128: return launch_tile<128, 128, 2, 2>(p, stream);
-    case TILE_128x256: return launch_tile<128, 256, 2, 2>(p, stream);
-    case TILE_256x224: return launch_tile<256, 224, 4, 1>(p, stream);
-    case TILE_128x64: return launch_tile<128, 64, 2, 2>(p, stream);
-    case TILE_64x64: return launch_tile<64, 64, 2, 2>(p, stream);
+    case TILE_256x256: return launch_tile<256, 256, 2, 2, 4>(p, path, stream);
+    case TILE_256x128: return launch_tile<256, 128, 2, 2, 5>(p, path, stream);
+    case TILE_128x128: return launch_tile<128, 128, 2, 2, 4>(p, path, stream);
+    case TILE_128x256: return launch_tile<128, 256, 2, 2, 5>(p, path, stream);
+    case TILE_256x224: return launch_tile<256, 224, 4, 1, 4>(p, path, stream);
+    case TILE_128x64: return launch_tile<128, 64, 2, 2, 4>(p, path, stream);
+    case TILE_64x64: return launch_tile<64, 64, 2, 2, 4>(p, path, stream);
     default: return hipErrorInvalidValue;
   }
 }

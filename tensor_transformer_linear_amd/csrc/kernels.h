@@ -48,7 +48,11 @@ enum GemmTile : int {
   TILE_COUNT = 7
 };
 
-hipError_t launch_gemm(const GemmProblem& p, int tile, hipStream_t stream);
+// Main-loop path: automatic (direct-to-LDS when there is no A transform and K % 32 == 0,
+// else register staging), or forced for testing.
+enum GemmPath : int { GEMM_PATH_AUTO = -1, GEMM_PATH_REGISTER = 0, GEMM_PATH_DMA = 1 };
+
+hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream);
 int gemm_pick_tile(int M, int N, int K);
 
 // RMSNorm statistics: r[m] = rsqrt(mean_k x^2 + eps) for every row, t[k] = bf16(1 + s[k]),

@@ -9,7 +9,7 @@
 // A workgroup owns ROWS weight rows that lie inside one chunk, over the whole K.
 // K is walked in slabs of 256: the weight slab (bf16, or E4M3 widened to bf16 on
 // the way in - E4M3 values are exactly bf16 values) and the matching x slab are
-// staged in LDS with 16-byte coalesced loads, the next slab's loads being in
+// staged in LDS with 16-byte coalesced loads, the next two slabs' loads being in
 // flight during the current slab's MFMAs. Each of the eight waves takes 32 of
 // the slab's K values for both 32-row blocks (x is the 32-row MFMA operand, the
 // weight rows the 32-column operand). With E4M3 weights each wave's 32 K values
@@ -57,9 +57,10 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { retur
 template <bool FP8>
 __global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, int tiles_per_chunk, int n_tiles,
                                                              int b0) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LM_WAVES * LM_ROWS * LM_BATCH * 4];  // 64 KB
-  unsigned char* sw = smem;                         // [64 rows][256] bf16
-  unsigned char* sx = smem + LM_ROWS * LM_ROWB;     // [32 rows][256] bf16
+  // Two slab buffers ([64 weight rows][256] + [32 x rows][256] bf16 each, 48 KB); the
+  // cross-wave reduction at the end reuses the same memory (64 KB).
+  constexpr int SLAB = (LM_ROWS + LM_BATCH) * LM_ROWB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SLAB];
   __shared__ float red_v[LM_THREADS / 64][LM_BATCH];
   __shared__ int red_i[LM_THREADS / 64][LM_BATCH];
   __shared__ int is_last;
@@ -79,16 +80,19 @@ __global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, in
   // bf16 weight: chunk q = tid + i * 512 -> row q / 32, 16-byte piece q % 32.
   // E4M3 weight: chunk q -> row q / 16, 16-byte piece q % 16 (16 K values).
   // x: chunk q -> batch row q / 32, piece q % 32.
-  u32x4_t rw[FP8 ? LM_W8CH : LM_WCH], rx[LM_XCH];
+  constexpr int NW = FP8 ? LM_W8CH : LM_WCH;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
+  // Loads of one slab into a register set (weight pieces rw, x pieces rx). Out-of-range
+  // pieces load from a valid address; lstore zeroes them, so nothing between the loads
+  // and lstore waits on them.
+  auto gload = [&](int k0, u32x4_t(&rw)[NW], u32x4_t(&rx)[LM_XCH]) {
     if constexpr (FP8) {
       const uint8_t* w8 = reinterpret_cast<const uint8_t*>(p.w);
 #pragma unroll
       for (int i = 0; i < LM_W8CH; ++i) {
         int q = tid + i * LM_THREADS, r = q >> 4, k = k0 + (q & 15) * 16;
         bool ok = r < nrows && k < K;
-        rw[i] = ok ? *reinterpret_cast<const u32x4_t*>(w8 + (int64_t)(row0 + r) * K + k) : zero;
+        rw[i] = *reinterpret_cast<const u32x4_t*>(w8 + (int64_t)(row0 + (ok ? r : 0)) * K + (ok ? k : 0));
       }
     } else {
       const uint16_t* w16 = reinterpret_cast<const uint16_t*>(p.w);
@@ -96,104 +100,120 @@ __global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, in
       for (int i = 0; i < LM_WCH; ++i) {
         int q = tid + i * LM_THREADS, r = q >> 5, k = k0 + (q & 31) * 8;
         bool ok = r < nrows && k < K;
-        rw[i] = ok ? *reinterpret_cast<const u32x4_t*>(w16 + (int64_t)(row0 + r) * K + k) : zero;
+        rw[i] = *reinterpret_cast<const u32x4_t*>(w16 + (int64_t)(row0 + (ok ? r : 0)) * K + (ok ? k : 0));
       }
     }
 #pragma unroll
     for (int i = 0; i < LM_XCH; ++i) {
       int q = tid + i * LM_THREADS, b = q >> 5, k = k0 + (q & 31) * 8;
       bool ok = b < nbatch && k < K;
-      rx[i] = ok ? *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(b0 + b) * K + k) : zero;
+      rx[i] = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(b0 + (ok ? b : 0)) * K + (ok ? k : 0));
     }
   };
-  auto lstore = [&]() {
+  // A register set into slab buffer `buf` (E4M3 widened to bf16 on the way).
+  auto lstore = [&](int buf, int k0, u32x4_t(&rw)[NW], u32x4_t(&rx)[LM_XCH]) {
+    unsigned char* sw = smem + buf * SLAB;
+    unsigned char* sx = sw + LM_ROWS * LM_ROWB;
     if constexpr (FP8) {
 #pragma unroll
       for (int i = 0; i < LM_W8CH; ++i) {
         int q = tid + i * LM_THREADS, r = q >> 4, c = (q & 15) * 2;
+        const u32x4_t w = (r < nrows && k0 + (q & 15) * 16 < K) ? rw[i] : zero;
         u32x4_t lo, hi;
-        lo[0] = e4m3x2_to_bf16x2<false>(rw[i][0]);
-        lo[1] = e4m3x2_to_bf16x2<true>(rw[i][0]);
-        lo[2] = e4m3x2_to_bf16x2<false>(rw[i][1]);
-        lo[3] = e4m3x2_to_bf16x2<true>(rw[i][1]);
-        hi[0] = e4m3x2_to_bf16x2<false>(rw[i][2]);
-        hi[1] = e4m3x2_to_bf16x2<true>(rw[i][2]);
-        hi[2] = e4m3x2_to_bf16x2<false>(rw[i][3]);
-        hi[3] = e4m3x2_to_bf16x2<true>(rw[i][3]);
+        lo[0] = e4m3x2_to_bf16x2<false>(w[0]);
+        lo[1] = e4m3x2_to_bf16x2<true>(w[0]);
+        lo[2] = e4m3x2_to_bf16x2<false>(w[1]);
+        lo[3] = e4m3x2_to_bf16x2<true>(w[1]);
+        hi[0] = e4m3x2_to_bf16x2<false>(w[2]);
+        hi[1] = e4m3x2_to_bf16x2<true>(w[2]);
+        hi[2] = e4m3x2_to_bf16x2<false>(w[3]);
+        hi[3] = e4m3x2_to_bf16x2<true>(w[3]);
         *reinterpret_cast<u32x4_t*>(sw + lm_off(r, c)) = lo;
         *reinterpret_cast<u32x4_t*>(sw + lm_off(r, c + 1)) = hi;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LM_WCH; ++i) {
-        int q = tid + i * LM_THREADS;
-        *reinterpret_cast<u32x4_t*>(sw + lm_off(q >> 5, q & 31)) = rw[i];
+        int q = tid + i * LM_THREADS, r = q >> 5;
+        *reinterpret_cast<u32x4_t*>(sw + lm_off(r, q & 31)) = (r < nrows && k0 + (q & 31) * 8 < K) ? rw[i] : zero;
       }
     }
 #pragma unroll
     for (int i = 0; i < LM_XCH; ++i) {
-      int q = tid + i * LM_THREADS;
-      *reinterpret_cast<u32x4_t*>(sx + lm_off(q >> 5, q & 31)) = rx[i];
+      int q = tid + i * LM_THREADS, b = q >> 5;
+      *reinterpret_cast<u32x4_t*>(sx + lm_off(b, q & 31)) = (b < nbatch && k0 + (q & 31) * 8 < K) ? rx[i] : zero;
     }
   };
 
   f32x16_t acc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+  static_for<2>([&](auto j) { static_for<16>([&](auto v) { acc[j][decltype(v)::value] = 0.0f; }); });
 
   const int nslab = (K + LM_KS - 1) / LM_KS;
   const int nblk = K / 128;
-  gload(0);
-  for (int s = 0; s < nslab; ++s) {
-    lstore();
-    __syncthreads();
-    if (s + 1 < nslab) gload((s + 1) * LM_KS);
-    // This wave's 32 K values of the slab: two k16 steps. Lane l supplies batch row
-    // (or weight row) l % 32 and eight K values starting at 8 * (l / 32).
+  // This wave's 32 K values of slab s: two k16 steps. Lane l supplies batch row (or weight
+  // row) l % 32 and eight K values starting at 8 * (l / 32).
+  auto compute = [&](int buf, int s) {
+    const unsigned char* sw = smem + buf * SLAB;
+    const unsigned char* sx = sw + LM_ROWS * LM_ROWB;
     f32x16_t part[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) part[j][v] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < LM_KW / 16; ++kk) {
+    if constexpr (FP8) static_for<2>([&](auto j) { static_for<16>([&](auto v) { part[j][decltype(v)::value] = 0.0f; }); });
+    static_for<LM_KW / 16>([&](auto kk) {
       const int c = (wave * LM_KW + kk * 16) / 8 + (lane >> 5);
       bf16x8_t xa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sx + lm_off(lane & 31, c)));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      static_for<2>([&](auto j) {
         bf16x8_t wb =
             __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sw + lm_off(j * 32 + (lane & 31), c)));
         if constexpr (FP8)
           part[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, wb, part[j], 0, 0, 0);
         else
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, wb, acc[j], 0, 0, 0);
-      }
-    }
+      });
+    });
     if constexpr (FP8) {
       const int blk = (s * LM_KS + wave * LM_KW) / 128;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      static_for<2>([&](auto j) {
         const int r = j * 32 + (lane & 31);
         const float sc = (r < nrows && blk < nblk) ? p.wscale[(int64_t)(row0 + r) * nblk + blk] : 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][v] = fmaf(part[j][v], sc, acc[j][v]);
-      }
+        static_for<16>([&](auto v) {
+          constexpr int vv = v;
+          acc[j][vv] = fmaf(part[j][vv], sc, acc[j][vv]);
+        });
+      });
     }
+  };
+
+  // Pipeline: two register sets carry slabs s + 1 and s + 2 from HBM while slab s is in
+  // LDS and being multiplied; one barrier per slab (the barrier of slab s also proves that
+  // every wave finished slab s - 2, whose buffer slab s overwrites).
+  // Loads are unconditional (slab index clamped to the last slab; the extra loads are
+  // in bounds and never stored) so the compiler keeps both sets in flight.
+  u32x4_t rw0[NW], rx0[LM_XCH], rw1[NW], rx1[LM_XCH];
+  auto slab_k = [&](int s) { return (s < nslab ? s : nslab - 1) * LM_KS; };
+  gload(slab_k(0), rw0, rx0);
+  gload(slab_k(1), rw1, rx1);
+  for (int s = 0; s < nslab; s += 2) {
+    lstore(0, s * LM_KS, rw0, rx0);
     __syncthreads();
+    gload(slab_k(s + 2), rw0, rx0);
+    compute(0, s);
+    if (s + 1 >= nslab) break;
+    lstore(1, (s + 1) * LM_KS, rw1, rx1);
+    __syncthreads();
+    gload(slab_k(s + 3), rw1, rx1);
+    compute(1, s + 1);
   }
+  __syncthreads();
 
   // Sum the eight waves' partials in wave order. Accumulator layout: lane l holds
   // weight row (column of the 32x32 block) l % 32 and batch rows 8(v/4) + 4(l/32) + v%4.
   float* red = reinterpret_cast<float*>(smem);  // [wave][batch 32][row 64]
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int b = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-      red[(wave * LM_BATCH + b) * LM_ROWS + j * 32 + (lane & 31)] = acc[j][v];
-    }
+  static_for<2>([&](auto j) {
+    static_for<16>([&](auto v) {
+      constexpr int vv = v;
+      const int b = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
+      red[(wave * LM_BATCH + b) * LM_ROWS + j * 32 + (lane & 31)] = acc[j][vv];
+    });
+  });
   __syncthreads();
   // Thread -> (batch b, rows r, r + 32 ... ): 512 threads cover 32 x 64 outputs, 4 each.
   {

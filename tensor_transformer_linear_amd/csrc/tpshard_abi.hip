@@ -15,6 +15,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local int g_tile_override = tpk::TILE_AUTO;
+thread_local int g_path_override = tpk::GEMM_PATH_AUTO;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -157,7 +158,7 @@ TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_s
                           ldy, &p);
   if (st != TP_OK) return st;
   if (M == 0) return ok();
-  return hip_status(tpk::launch_gemm(p, g_tile_override, as_stream(stream)), "tp_column_linear launch");
+  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_column_linear launch");
 }
 
 TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
@@ -195,7 +196,7 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
   p.ep.act = TP_ACT_NONE;
   p.ep.out_f32 = 1;
   p.ep.accumulate = accumulate;
-  return hip_status(tpk::launch_gemm(p, g_tile_override, as_stream(stream)), "tp_row_linear_partial launch");
+  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_row_linear_partial launch");
 }
 
 TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K) {
@@ -236,7 +237,7 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
     p.row_r = r;
     p.col_t = scale ? t : nullptr;
   }
-  return hip_status(tpk::launch_gemm(p, g_tile_override, s), "rmsnorm_column_linear GEMM launch");
+  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, s), "rmsnorm_column_linear GEMM launch");
 }
 
 TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk) {
@@ -299,6 +300,12 @@ TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t voc
 TP_API int tp_debug_set_gemm_tile(int tile) {
   if (tile < tpk::TILE_AUTO || tile >= tpk::TILE_COUNT) return fail(TP_ERR_INVALID_ARG, "unknown tile %d", tile);
   g_tile_override = tile;
+  return ok();
+}
+
+TP_API int tp_debug_set_gemm_path(int path) {
+  if (path < tpk::GEMM_PATH_AUTO || path > tpk::GEMM_PATH_DMA) return fail(TP_ERR_INVALID_ARG, "unknown path %d", path);
+  g_path_override = path;
   return ok();
 }
 

@@ -13,10 +13,14 @@ pytestmark = pytest.mark.gpu
 TILES = sorted(tt.GEMM_TILES)
 
 
+PATHS = [tt.GEMM_PATH_REGISTER, tt.GEMM_PATH_DMA]
+
+
 @pytest.fixture(autouse=True)
 def _reset_tile():
     yield
     tt.set_gemm_tile(-1)
+    tt.set_gemm_path(-1)
 
 
 def _int_inputs(M, K, sizes, tp, rank, seed):
@@ -27,12 +31,15 @@ def _int_inputs(M, K, sizes, tp, rank, seed):
     return x, w, b, np.ascontiguousarray(w[rows]), np.ascontiguousarray(b[rows])
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("tile", [-1] + TILES)
-def test_column_linear_integer_exact_every_tile(tile):
+def test_column_linear_integer_exact_every_tile(tile, path):
     """Integer inputs make every f32 sum exact: the GPU must match the oracle bit for bit.
-    Ragged M, N and K; a sub-parameter boundary falls inside tiles."""
+    Ragged M and N, a sub-parameter boundary inside tiles; K = 200 (ragged against the
+    register path's 64-wide steps) or K = 224 (seven 32-wide direct-to-LDS steps)."""
     tt.set_gemm_tile(tile)
-    M, K, sizes, tp, rank = 301, 200, [300, 76, 76], 2, 1
+    tt.set_gemm_path(path)
+    M, K, sizes, tp, rank = 301, (224 if path == tt.GEMM_PATH_DMA else 200), [300, 76, 76], 2, 1
     x, w, b, w_r, b_r = _int_inputs(M, K, sizes, tp, rank, 10 + max(tile, 0))
     X, W, B = dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r)
     y = tt.tp_column_linear(X, W, B, sizes, tp, rank)
@@ -52,11 +59,13 @@ def test_column_linear_integer_exact_every_tile(tile):
     assert np.all(got[:, sum(sizes):] == sentinel)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("tile", [-1, 0, 4, 6])
-def test_column_linear_gaussian_gelu(tile):
+def test_column_linear_gaussian_gelu(tile, path):
     tt.set_gemm_tile(tile)
+    tt.set_gemm_path(path)
     g = np.random.default_rng(5)
-    M, K, sizes, tp, rank = 260, 456, [512, 128, 128], 8, 0
+    M, K, sizes, tp, rank = 260, (448 if path == tt.GEMM_PATH_DMA else 456), [512, 128, 128], 8, 0
     x = synth.bf16_from_float(g.standard_normal((M, K)))
     w_r = synth.bf16_from_float(g.standard_normal((96, K)) * 0.05)
     b_r = synth.bf16_from_float(g.standard_normal(96) * 0.05)
@@ -93,8 +102,11 @@ def test_gelu_every_finite_bf16():
     assert np.count_nonzero(~same) <= 0.002 * M
 
 
-def test_row_partial_integer_exact_and_rank_sum():
-    M, Kl, N, tp = 130, 3 * 104, 200, 3  # K_r = 104: one full 64-wide K step and a ragged one
+@pytest.mark.parametrize("path", PATHS)
+def test_row_partial_integer_exact_and_rank_sum(path):
+    tt.set_gemm_path(path)
+    # K_r = 104: one full 64-wide step and a ragged one; K_r = 96: three 32-wide DMA steps
+    M, Kl, N, tp = 130, 3 * (96 if path == tt.GEMM_PATH_DMA else 104), 200, 3
     x = synth.bf16_integers((M, Kl), -3, 3, 50)
     w = synth.bf16_integers((N, Kl), -3, 3, 51)
     b = synth.bf16_integers((N,), -8, 8, 52)
@@ -140,9 +152,11 @@ def test_mlp_gpt2_small_tp2_both_ranks():
     assert_close(host_f32(S), full, what="rank sum vs unsharded MLP")
 
 
-def test_column_shards_assemble_bitwise_to_unsharded():
+@pytest.mark.parametrize("path", PATHS)
+def test_column_shards_assemble_bitwise_to_unsharded(path):
     """All eight ranks' LOGICAL outputs together equal the tp=1 output bit for bit (the same
     K order reaches every output element whatever the N tiling)."""
+    tt.set_gemm_path(path)
     sizes, tp = [4096, 1024, 1024], 8
     M, K = 192, 4096
     g = np.random.default_rng(9)
