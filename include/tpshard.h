@@ -137,9 +137,14 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
                           void* stream);
 
 /*
- * tp_rmsnorm_workspace_bytes - device workspace rmsnorm_column_linear needs for M rows of K.
+ * tp_rmsnorm_workspace_bytes     device workspace for rmsnorm_column_linear's fast path: the
+ *                                row statistics plus the bf16 normalised rows [M, K], which the
+ *                                GEMM then reads with direct-to-LDS loads.
+ * tp_rmsnorm_workspace_min_bytes the least workspace it accepts (row statistics only): the
+ *                                normalisation is then fused into the GEMM's A staging.
  */
 TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K);
+TP_API size_t tp_rmsnorm_workspace_min_bytes(int64_t M, int64_t K);
 
 /*
  * rmsnorm_column_linear - RMSNorm of each input row, then the rank's column linear on it.
@@ -157,8 +162,11 @@ TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K);
  * xnorm_out  device bf16 [M, K] receiving y, or NULL
  * w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, y, y_dtype, layout, ldy:
  *            as tp_column_linear, with y's input rows being the normalised rows
- * workspace  device, at least tp_rmsnorm_workspace_bytes(M, K) bytes, 256-byte aligned;
- *            contents need no initialisation and are scratch between calls
+ * workspace  device, 256-byte aligned, contents need no initialisation (scratch between
+ *            calls). With xnorm_out, or with tp_rmsnorm_workspace_bytes(M, K) bytes, the
+ *            normalised rows are materialised and multiplied; with at least
+ *            tp_rmsnorm_workspace_min_bytes(M, K) bytes the normalisation is fused into the
+ *            GEMM's A staging. Both give bit-identical y.
  * Errors: as tp_column_linear, TP_ERR_SHAPE for a short workspace.
  */
 TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
@@ -190,9 +198,11 @@ TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, 
  * logits            device f32 [B, V_r]; chunk c's rows land at columns c*max_rows_per_chunk...
  * argmax_local      device int32 [B]: lowest local index of the row's largest logit
  * max_logit         device f32 [B] or NULL: that largest logit
- * workspace         device, tp_lm_head_workspace_bytes(...) bytes, 256-byte aligned. Zero
- *                   it once before the first call; every call leaves it zeroed again.
- *                   Calls that overlap in time must not share a workspace.
+ * workspace         device, tp_lm_head_workspace_bytes(...) bytes, 256-byte aligned; needs
+ *                   no initialisation (per-workgroup argmax candidates, scratch between
+ *                   calls). Calls that overlap in time must not share a workspace.
+ * Two kernels run per 32 batch rows: the logits with per-workgroup argmax candidates,
+ * then the candidates' reduction.
  * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE (chunk size <= 0, workspace short),
  * TP_ERR_UNSUPPORTED (K % 8, fp8 with K % 128, dtype), TP_ERR_HIP.
  */
@@ -223,10 +233,14 @@ TP_API const char* tp_version(void);
  *                          automatic, 0 register-staged operands, 1 direct-to-LDS loads
  *                          (needs K % 32 == 0 and no RMSNorm transform; a call that cannot
  *                          use it returns TP_ERR_HIP).
+ * tp_debug_set_lm_head_shape forces the LM head's launch shape on this thread: -1 default,
+ *                          0..5 (16-row weight groups per workgroup, waves, K steps per load
+ *                          batch) = (4,8,8) (2,8,8) (4,4,8) (2,4,8) (4,8,4) (1,8,8).
  * tp_debug_gemm_pick_tile  the automatic choice for an M x N x K problem (-1 if invalid).
  */
 TP_API int tp_debug_set_gemm_tile(int tile);
 TP_API int tp_debug_set_gemm_path(int path);
+TP_API int tp_debug_set_lm_head_shape(int shape);
 TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -32,6 +32,7 @@ SIGNATURES = {
     "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int, _int, _i64, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _int, _vp, _int, _vp]),
     "tp_rmsnorm_workspace_bytes": (_sz, [_i64, _i64]),
+    "tp_rmsnorm_workspace_min_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_column_linear": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _P64, _int, _int, _int,
                                      _vp, _int, _int, _i64, _vp, _sz, _vp]),
     "tp_lm_head_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _i64]),
@@ -41,6 +42,7 @@ SIGNATURES = {
     "tp_version": (ctypes.c_char_p, []),
     "tp_debug_set_gemm_tile": (_int, [_int]),
     "tp_debug_set_gemm_path": (_int, [_int]),
+    "tp_debug_set_lm_head_shape": (_int, [_int]),
     "tp_debug_gemm_pick_tile": (_int, [_i64, _i64, _i64]),
 }
 
@@ -137,10 +139,17 @@ def tp_rmsnorm_workspace_bytes(M: int, K: int) -> int:
     return int(lib().tp_rmsnorm_workspace_bytes(M, K))
 
 
+def tp_rmsnorm_workspace_min_bytes(M: int, K: int) -> int:
+    return int(lib().tp_rmsnorm_workspace_min_bytes(M, K))
+
+
 def rmsnorm_column_linear(x, scale, eps, w_shard, bias_shard, subparam_sizes, tp_size, rank, xnorm_out=None,
                           y=None, y_dtype=TP_DTYPE_BF16, layout=TP_LAYOUT_LOCAL, ldy=None, workspace=None,
                           stream=None):
-    """RMSNorm rows of ``x`` (optionally into ``xnorm_out``), then the rank's column linear; returns ``y``."""
+    """RMSNorm rows of ``x`` (optionally into ``xnorm_out``), then the rank's column linear; returns ``y``.
+
+    Without ``workspace`` a workspace of ``tp_rmsnorm_workspace_bytes`` (fast, materialised
+    path) is allocated; pass one of ``tp_rmsnorm_workspace_min_bytes`` for the fused path."""
     M, K = x.shape
     sizes, n = _i64_array(subparam_sizes)
     if y is None:
@@ -163,7 +172,7 @@ def tp_lm_head_workspace_bytes(B, vocab, tp_size, rank, max_rows_per_chunk) -> i
 
 
 def lm_head_workspace(B, vocab, tp_size, rank, max_rows_per_chunk, device="cuda"):
-    """A zeroed workspace for ``lm_head_shard_argmax`` (every call leaves it zeroed)."""
+    """A workspace for ``lm_head_shard_argmax`` (scratch; zeroed here only for tidiness)."""
     n = tp_lm_head_workspace_bytes(B, vocab, tp_size, rank, max_rows_per_chunk)
     if n == 0:
         raise TpError(TP_ERR_INVALID_ARG, "invalid LM-head workspace query")
@@ -202,6 +211,14 @@ def set_gemm_path(path: int) -> None:
 
 
 GEMM_PATH_AUTO, GEMM_PATH_REGISTER, GEMM_PATH_DMA = -1, 0, 1
+
+
+def set_lm_head_shape(shape: int) -> None:
+    """Force the LM head's launch shape on this thread (-1 = default); for tests and tuning."""
+    _check(lib().tp_debug_set_lm_head_shape(shape))
+
+
+LM_HEAD_SHAPES = {0: (4, 8, 8), 1: (2, 8, 8), 2: (4, 4, 8), 3: (2, 4, 8), 4: (4, 8, 4), 5: (1, 8, 8)}
 
 
 def gemm_pick_tile(M: int, N: int, K: int) -> int:

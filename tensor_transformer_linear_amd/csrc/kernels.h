@@ -73,6 +73,8 @@ struct LmHeadProblem {
   void* workspace;
 };
 size_t lm_head_workspace_bytes(int B, int V, int chunk);
-hipError_t launch_lm_head(const LmHeadProblem& p, hipStream_t stream);
+int lm_head_shape_count();
+// shape: -1 = default launch shape, else an index into the LM head's shape table (tuning).
+hipError_t launch_lm_head(const LmHeadProblem& p, int shape, hipStream_t stream);
 
 }  // namespace tpk

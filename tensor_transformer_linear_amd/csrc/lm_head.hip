@@ -6,19 +6,22 @@
 // logits. Decode has a few batch rows, so the work is a stream of the weight
 // shard from HBM: every weight byte is read once.
 //
-// A workgroup owns ROWS weight rows that lie inside one chunk, over the whole K.
-// K is walked in slabs of 256: the weight slab (bf16, or E4M3 widened to bf16 on
-// the way in - E4M3 values are exactly bf16 values) and the matching x slab are
-// staged in LDS with 16-byte coalesced loads, the next two slabs' loads being in
-// flight during the current slab's MFMAs. Each of the eight waves takes 32 of
-// the slab's K values for both 32-row blocks (x is the 32-row MFMA operand, the
-// weight rows the 32-column operand). With E4M3 weights each wave's 32 K values
-// lie inside one 128-wide scale block, so the wave multiplies its block partial
-// by the row's scale before adding it to its float32 accumulator. The eight
-// waves' partials are summed through LDS in a fixed order, written as logits,
-// and reduced to a (max, lowest index) pair per batch row; the last workgroup
-// to finish (a device-scope ticket) reduces the pairs of all workgroups and
-// resets the ticket.
+// A workgroup owns 16 G weight rows that lie inside one chunk, over the whole K;
+// its waves split K. Each wave streams its K range straight from global
+// memory into MFMA operand registers (no LDS staging, no barriers in the loop):
+// for every 32-wide K step it loads the 16-byte pieces of the G 16-row weight
+// groups and of the two 16-row x groups and issues v_mfma_f32_16x16x32_bf16 with
+// x as the row operand and the weight as the column operand, so every lane's
+// accumulators belong to one weight row. Steps go in batches of P, each issued
+// whole before it is multiplied. E4M3 weights are widened to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, every E4M3 value is a bf16
+// value) and each 128-wide K block's partial is multiplied by the row's block
+// scale before it joins the float32 accumulator. The waves' partials are
+// summed through LDS in wave order (deterministic), written as logits, and
+// reduced to a (max, lowest index) pair per batch row; a second kernel
+// launched right after reduces the pairs of all workgroups (a kernel boundary
+// instead of per-workgroup device-scope fences, which on gfx950 write back and
+// invalidate the whole L2).
 #include "common.h"
 #include "kernels.h"
 
@@ -26,23 +29,16 @@ namespace tpk {
 
 namespace {
 
-constexpr int LM_ROWS = 64;        // weight rows per workgroup (two 32-row MFMA blocks)
-constexpr int LM_BATCH = 32;       // batch rows handled per launch pass (the MFMA's 32-row operand)
-constexpr int LM_KS = 256;         // K per slab
-constexpr int LM_THREADS = 512;    // eight waves
-constexpr int LM_WAVES = LM_THREADS / 64;
-constexpr int LM_KW = LM_KS / LM_WAVES;  // K values per wave per slab (32)
-constexpr int LM_ROWB = LM_KS * 2;       // LDS bytes per staged row (bf16)
-constexpr int LM_WCH = LM_ROWS * LM_KS / 8 / LM_THREADS;    // weight 16-byte chunks per thread (bf16)
-constexpr int LM_XCH = LM_BATCH * LM_KS / 8 / LM_THREADS;   // x chunks per thread
-constexpr int LM_W8CH = LM_ROWS * LM_KS / 16 / LM_THREADS;  // weight 16-byte chunks per thread (E4M3)
-constexpr size_t LM_TICKET_BYTES = 256;
+constexpr int LM_BATCH = 32;  // batch rows per launch pass (two 16-row MFMA groups)
+constexpr int LM_FIN_THREADS = 256;
 
-static_assert(LM_WCH == 4 && LM_XCH == 2 && LM_W8CH == 2, "slab partition");
-
-// LDS offset of 16-byte chunk c (0..31) of staged row `row`; the XOR spreads the
-// rows read by one ds_read_b128 phase over all banks.
-__device__ __forceinline__ int lm_off(int row, int c) { return row * LM_ROWB + ((c ^ (row & 31)) << 4); }
+// Launch shapes: G 16-row weight groups per workgroup, W waves splitting K, P 32-wide K steps
+// per batch of loads (a multiple of four: whole 128-wide E4M3 blocks).
+struct LmShape {
+  int G, W, P;
+};
+constexpr LmShape kLmShapes[] = {{4, 8, 8}, {2, 8, 8}, {4, 4, 8}, {2, 4, 8}, {4, 8, 4}, {1, 8, 8}};
+constexpr int kLmDefaultShape = 4;
 
 // Two E4M3 codes (bytes HI ? 2,3 : 0,1 of w) -> two bf16, exactly (scale 1).
 template <bool HI>
@@ -54,16 +50,14 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-template <bool FP8>
-__global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, int tiles_per_chunk, int n_tiles,
-                                                             int b0) {
-  // Two slab buffers ([64 weight rows][256] + [32 x rows][256] bf16 each, 48 KB); the
-  // cross-wave reduction at the end reuses the same memory (64 KB).
-  constexpr int SLAB = (LM_ROWS + LM_BATCH) * LM_ROWB;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * SLAB];
-  __shared__ float red_v[LM_THREADS / 64][LM_BATCH];
-  __shared__ int red_i[LM_THREADS / 64][LM_BATCH];
-  __shared__ int is_last;
+template <bool FP8, int G, int LM_WAVES, int LM_P>
+__global__ __launch_bounds__(LM_WAVES * 64) void lm_head_kernel(LmHeadProblem p, int tiles_per_chunk, int n_tiles,
+                                                               int b0) {
+  constexpr int LM_ROWS = G * 16;
+  constexpr int LM_THREADS = LM_WAVES * 64;
+  __shared__ __attribute__((aligned(16))) float red[LM_WAVES * LM_BATCH * LM_ROWS];
+  __shared__ float red_v[LM_WAVES][LM_BATCH];
+  __shared__ int red_i[LM_WAVES][LM_BATCH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.K, V = p.V, C = p.chunk;
@@ -76,160 +70,173 @@ __global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, in
   const int chunk_end = min(V, (chunk + 1) * C);
   const int nrows = max(0, min(LM_ROWS, chunk_end - row0));
 
-  // Global-load assignment.
-  // bf16 weight: chunk q = tid + i * 512 -> row q / 32, 16-byte piece q % 32.
-  // E4M3 weight: chunk q -> row q / 16, 16-byte piece q % 16 (16 K values).
-  // x: chunk q -> batch row q / 32, piece q % 32.
-  constexpr int NW = FP8 ? LM_W8CH : LM_WCH;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // Loads of one slab into a register set (weight pieces rw, x pieces rx). Out-of-range
-  // pieces load from a valid address; lstore zeroes them, so nothing between the loads
-  // and lstore waits on them.
-  auto gload = [&](int k0, u32x4_t(&rw)[NW], u32x4_t(&rx)[LM_XCH]) {
-    if constexpr (FP8) {
-      const uint8_t* w8 = reinterpret_cast<const uint8_t*>(p.w);
-#pragma unroll
-      for (int i = 0; i < LM_W8CH; ++i) {
-        int q = tid + i * LM_THREADS, r = q >> 4, k = k0 + (q & 15) * 16;
-        bool ok = r < nrows && k < K;
-        rw[i] = *reinterpret_cast<const u32x4_t*>(w8 + (int64_t)(row0 + (ok ? r : 0)) * K + (ok ? k : 0));
-      }
-    } else {
-      const uint16_t* w16 = reinterpret_cast<const uint16_t*>(p.w);
-#pragma unroll
-      for (int i = 0; i < LM_WCH; ++i) {
-        int q = tid + i * LM_THREADS, r = q >> 5, k = k0 + (q & 31) * 8;
-        bool ok = r < nrows && k < K;
-        rw[i] = *reinterpret_cast<const u32x4_t*>(w16 + (int64_t)(row0 + (ok ? r : 0)) * K + (ok ? k : 0));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < LM_XCH; ++i) {
-      int q = tid + i * LM_THREADS, b = q >> 5, k = k0 + (q & 31) * 8;
-      bool ok = b < nbatch && k < K;
-      rx[i] = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(b0 + (ok ? b : 0)) * K + (ok ? k : 0));
-    }
-  };
-  // A register set into slab buffer `buf` (E4M3 widened to bf16 on the way).
-  auto lstore = [&](int buf, int k0, u32x4_t(&rw)[NW], u32x4_t(&rx)[LM_XCH]) {
-    unsigned char* sw = smem + buf * SLAB;
-    unsigned char* sx = sw + LM_ROWS * LM_ROWB;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < LM_W8CH; ++i) {
-        int q = tid + i * LM_THREADS, r = q >> 4, c = (q & 15) * 2;
-        const u32x4_t w = (r < nrows && k0 + (q & 15) * 16 < K) ? rw[i] : zero;
-        u32x4_t lo, hi;
-        lo[0] = e4m3x2_to_bf16x2<false>(w[0]);
-        lo[1] = e4m3x2_to_bf16x2<true>(w[0]);
-        lo[2] = e4m3x2_to_bf16x2<false>(w[1]);
-        lo[3] = e4m3x2_to_bf16x2<true>(w[1]);
-        hi[0] = e4m3x2_to_bf16x2<false>(w[2]);
-        hi[1] = e4m3x2_to_bf16x2<true>(w[2]);
-        hi[2] = e4m3x2_to_bf16x2<false>(w[3]);
-        hi[3] = e4m3x2_to_bf16x2<true>(w[3]);
-        *reinterpret_cast<u32x4_t*>(sw + lm_off(r, c)) = lo;
-        *reinterpret_cast<u32x4_t*>(sw + lm_off(r, c + 1)) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < LM_WCH; ++i) {
-        int q = tid + i * LM_THREADS, r = q >> 5;
-        *reinterpret_cast<u32x4_t*>(sw + lm_off(r, q & 31)) = (r < nrows && k0 + (q & 31) * 8 < K) ? rw[i] : zero;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < LM_XCH; ++i) {
-      int q = tid + i * LM_THREADS, b = q >> 5;
-      *reinterpret_cast<u32x4_t*>(sx + lm_off(b, q & 31)) = (b < nbatch && k0 + (q & 31) * 8 < K) ? rx[i] : zero;
-    }
-  };
-
-  f32x16_t acc[2];
-  static_for<2>([&](auto j) { static_for<16>([&](auto v) { acc[j][decltype(v)::value] = 0.0f; }); });
-
-  const int nslab = (K + LM_KS - 1) / LM_KS;
+  // This wave's K steps [s_begin, s_end) of the ceil(K / 32) steps, in whole 128-wide
+  // blocks (four steps), so that an E4M3 scale block never straddles two waves.
+  const int nsteps = (K + 31) / 32;
+  const int per_wave = ((nsteps + LM_WAVES - 1) / LM_WAVES + 3) / 4 * 4;
+  const int s_begin = min(nsteps, wave * per_wave), s_end = min(nsteps, s_begin + per_wave);
   const int nblk = K / 128;
-  // This wave's 32 K values of slab s: two k16 steps. Lane l supplies batch row (or weight
-  // row) l % 32 and eight K values starting at 8 * (l / 32).
-  auto compute = [&](int buf, int s) {
-    const unsigned char* sw = smem + buf * SLAB;
-    const unsigned char* sx = sw + LM_ROWS * LM_ROWB;
-    f32x16_t part[2];
-    if constexpr (FP8) static_for<2>([&](auto j) { static_for<16>([&](auto v) { part[j][decltype(v)::value] = 0.0f; }); });
-    static_for<LM_KW / 16>([&](auto kk) {
-      const int c = (wave * LM_KW + kk * 16) / 8 + (lane >> 5);
-      bf16x8_t xa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sx + lm_off(lane & 31, c)));
-      static_for<2>([&](auto j) {
-        bf16x8_t wb =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sw + lm_off(j * 32 + (lane & 31), c)));
-        if constexpr (FP8)
-          part[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, wb, part[j], 0, 0, 0);
-        else
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, wb, acc[j], 0, 0, 0);
-      });
+
+  // Lane roles in v_mfma_f32_16x16x32_bf16: lane l supplies row (or column) l % 16 and
+  // eight K values selected by q = l / 16. Weight rows and x rows beyond the tile read a
+  // clamped row: they only feed outputs that are never stored.
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int64_t ldw = FP8 ? (int64_t)K : 2 * (int64_t)K;  // bytes per weight row
+  const unsigned char* wrow[G];
+  bool wok[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int r = g * 16 + r16;
+    wok[g] = r < nrows;
+    wrow[g] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)(row0 + (wok[g] ? r : 0)) * ldw;
+  }
+  const uint16_t* xrow[2];
+  bool xok[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = h * 16 + r16;
+    xok[h] = b < nbatch;
+    xrow[h] = p.x + (int64_t)(b0 + (xok[h] ? b : 0)) * K;
+  }
+
+  // K values of step st seen by this lane (8 consecutive from kofs(st)). bf16: the natural
+  // layout, 32 st + 8 q. E4M3: one 16-byte weight piece holds K values 64 (st / 2) + 16 q ..
+  // +16; its first eight feed the even step, the other eight the odd step.
+  auto kofs = [&](int st) { return FP8 ? (st & ~1) * 32 + kq * 16 + (st & 1) * 8 : st * 32 + kq * 8; };
+
+  constexpr int WPIECES = FP8 ? LM_P / 2 : LM_P;
+  struct Batch {
+    u32x4_t w[WPIECES][G];
+    u32x4_t x[LM_P][2];
+    float sc[LM_P / 4][G];
+  };
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  // Issues the loads of the batch starting at step s0 (clamped to the last steps, so the
+  // loads are unconditional and stay in flight; consume ignores steps past s_end).
+  auto load = [&](int s0, Batch& bt) {
+    static_for<LM_P>([&](auto i) {
+      const int st = min(s0 + (int)i, nsteps - 1);
+      const int k = kofs(st) < K ? kofs(st) : 0;
+      static_for<2>([&](auto h) { bt.x[i][h] = *reinterpret_cast<const u32x4_t*>(xrow[h] + k); });
+    });
+    static_for<WPIECES>([&](auto i) {
+      int off;
+      if constexpr (FP8) {
+        off = min(s0 + 2 * (int)i, nsteps - 2) * 32 + kq * 16;
+      } else {
+        const int k = kofs(min(s0 + (int)i, nsteps - 1));
+        off = (k < K ? k : 0) * 2;
+      }
+      static_for<G>([&](auto g) { bt.w[i][g] = *reinterpret_cast<const u32x4_t*>(wrow[g] + off); });
     });
     if constexpr (FP8) {
-      const int blk = (s * LM_KS + wave * LM_KW) / 128;
-      static_for<2>([&](auto j) {
-        const int r = j * 32 + (lane & 31);
-        const float sc = (r < nrows && blk < nblk) ? p.wscale[(int64_t)(row0 + r) * nblk + blk] : 0.0f;
-        static_for<16>([&](auto v) {
-          constexpr int vv = v;
-          acc[j][vv] = fmaf(part[j][vv], sc, acc[j][vv]);
+      static_for<LM_P / 4>([&](auto j) {
+        const int blk = min(s0 / 4 + (int)j, nblk - 1);
+        static_for<G>([&](auto g) {
+          bt.sc[j][g] = p.wscale[(int64_t)(row0 + (wok[g] ? g * 16 + r16 : 0)) * nblk + blk];
         });
       });
     }
   };
 
-  // Pipeline: two register sets carry slabs s + 1 and s + 2 from HBM while slab s is in
-  // LDS and being multiplied; one barrier per slab (the barrier of slab s also proves that
-  // every wave finished slab s - 2, whose buffer slab s overwrites).
-  // Loads are unconditional (slab index clamped to the last slab; the extra loads are
-  // in bounds and never stored) so the compiler keeps both sets in flight.
-  u32x4_t rw0[NW], rx0[LM_XCH], rw1[NW], rx1[LM_XCH];
-  auto slab_k = [&](int s) { return (s < nslab ? s : nslab - 1) * LM_KS; };
-  gload(slab_k(0), rw0, rx0);
-  gload(slab_k(1), rw1, rx1);
-  for (int s = 0; s < nslab; s += 2) {
-    lstore(0, s * LM_KS, rw0, rx0);
-    __syncthreads();
-    gload(slab_k(s + 2), rw0, rx0);
-    compute(0, s);
-    if (s + 1 >= nslab) break;
-    lstore(1, (s + 1) * LM_KS, rw1, rx1);
-    __syncthreads();
-    gload(slab_k(s + 3), rw1, rx1);
-    compute(1, s + 1);
-  }
-  __syncthreads();
+  f32x4_t acc[G][2], part[G][2];
+  auto clear = [&](f32x4_t(&a)[G][2]) {
+    static_for<G>([&](auto g) {
+      static_for<2>([&](auto h) { static_for<4>([&](auto v) { a[g][h][decltype(v)::value] = 0.0f; }); });
+    });
+  };
+  clear(acc);
+  clear(part);
+  // Multiplies the batch starting at step s0. Steps at or past s_end multiply zeros instead
+  // of branching around the MFMAs (a branch would make the compiler drain the loads in
+  // flight at the join). With E4M3 weights, each 128-wide block's partial (four steps) is
+  // scaled by the row's block scale as it joins the float32 accumulator.
+  auto consume = [&](int s0, const Batch& bt) {
+    static_for<LM_P>([&](auto i) {
+      constexpr int ii = i;
+      const int st = s0 + ii;
+      const bool kok = st < s_end && kofs(st) < K;
+      bf16x8_t xa[2];
+      static_for<2>([&](auto h) { xa[h] = __builtin_bit_cast(bf16x8_t, (kok && xok[h]) ? bt.x[i][h] : zero); });
+      static_for<G>([&](auto g) {
+        u32x4_t wv;
+        if constexpr (FP8) {
+          const u32x4_t q = bt.w[ii / 2][g];
+          constexpr int o = (ii % 2) * 2;  // dwords 0,1 feed the even step, 2,3 the odd
+          wv[0] = e4m3x2_to_bf16x2<false>(q[o]);
+          wv[1] = e4m3x2_to_bf16x2<true>(q[o]);
+          wv[2] = e4m3x2_to_bf16x2<false>(q[o + 1]);
+          wv[3] = e4m3x2_to_bf16x2<true>(q[o + 1]);
+        } else {
+          wv = bt.w[i][g];
+        }
+        const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wv);
+        static_for<2>([&](auto h) {
+          if constexpr (FP8)
+            part[g][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[h], wb, part[g][h], 0, 0, 0);
+          else
+            acc[g][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[h], wb, acc[g][h], 0, 0, 0);
+        });
+      });
+      if constexpr (FP8 && ii % 4 == 3) {
+        const bool live = s0 + ii - 3 < s_end;
+        static_for<G>([&](auto g) {
+          const float sc = (live && wok[g]) ? bt.sc[ii / 4][g] : 0.0f;
+          static_for<2>([&](auto h) {
+            static_for<4>([&](auto v) {
+              constexpr int vv = v;
+              acc[g][h][vv] = fmaf(part[g][h][vv], sc, acc[g][h][vv]);
+            });
+          });
+        });
+        clear(part);
+      }
+    });
+  };
 
-  // Sum the eight waves' partials in wave order. Accumulator layout: lane l holds
-  // weight row (column of the 32x32 block) l % 32 and batch rows 8(v/4) + 4(l/32) + v%4.
-  float* red = reinterpret_cast<float*>(smem);  // [wave][batch 32][row 64]
-  static_for<2>([&](auto j) {
-    static_for<16>([&](auto v) {
-      constexpr int vv = v;
-      const int b = (vv >> 2) * 8 + (lane >> 5) * 4 + (vv & 3);
-      red[(wave * LM_BATCH + b) * LM_ROWS + j * 32 + (lane & 31)] = acc[j][vv];
+  // One batch in flight per wave, issued whole (eight steps: 48 KB per wave, 384 KB per
+  // workgroup), then multiplied. The eight waves of the CU keep HBM busy between them.
+  for (int s0 = s_begin; s0 < s_end; s0 += LM_P) {
+    Batch bt;
+    load(s0, bt);
+    // keeps the scheduler from interleaving the batch's loads with its MFMAs (which would
+    // leave only a few loads in flight per wave)
+    __builtin_amdgcn_sched_barrier(0);
+    consume(s0, bt);
+  }
+
+  // Sum the eight waves' partials in wave order. 16x16 accumulator layout: lane l holds
+  // weight row (block column) l % 16 and batch rows 4 (l / 16) + v of its four values.
+  static_for<G>([&](auto g) {
+    static_for<2>([&](auto h) {
+      static_for<4>([&](auto v) {
+        constexpr int vv = v;
+        const int b = h * 16 + kq * 4 + vv;
+        red[(wave * LM_BATCH + b) * LM_ROWS + g * 16 + r16] = acc[g][h][vv];
+      });
     });
   });
   __syncthreads();
-  // Thread -> (batch b, rows r, r + 32 ... ): 512 threads cover 32 x 64 outputs, 4 each.
+  // Thread -> weight row r = tid % LM_ROWS and batch rows bq, bq + BSTEP, ...: the threads
+  // cover the 32 x LM_ROWS outputs. Per batch row, the LM_ROWS threads holding it (whole
+  // waves, or a wave's aligned quarter/half for 16/32 rows) reduce to this workgroup's
+  // (max, lowest index) candidate.
+  constexpr int BSTEP = LM_THREADS / LM_ROWS;  // batch rows handled side by side
+  constexpr int BITER = LM_BATCH / BSTEP;
+  static_assert(LM_ROWS <= 64 && BITER * BSTEP == LM_BATCH, "reduction layout");
   {
-    const int r = tid & 63, bq = tid >> 6;  // batch rows bq, bq + 8, bq + 16, bq + 24
+    const int r = tid % LM_ROWS, bq = tid / LM_ROWS;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int b = bq + 8 * t;
+    for (int t = 0; t < BITER; ++t) {
+      const int b = bq + BSTEP * t;
       float sum = 0.0f;
 #pragma unroll
       for (int w = 0; w < LM_WAVES; ++w) sum += red[(w * LM_BATCH + b) * LM_ROWS + r];
       if (r < nrows && b < nbatch) p.logits[(int64_t)(b0 + b) * V + row0 + r] = sum;
       float v = (r < nrows && !(sum != sum)) ? sum : -INFINITY;
       int idx = row0 + r;
-      // wave-wide (max, lowest index) over the 64 rows of batch row b
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
+      for (int off = LM_ROWS / 2; off > 0; off >>= 1) {
         float ov = __shfl_xor(v, off, 64);
         int oi = __shfl_xor(idx, off, 64);
         if (better(ov, oi, v, idx)) {
@@ -237,88 +244,122 @@ __global__ __launch_bounds__(LM_THREADS) void lm_head_kernel(LmHeadProblem p, in
           idx = oi;
         }
       }
-      if (lane == 0) {
-        red_v[wave][t] = v;
-        red_i[wave][t] = idx;
+      if (r == 0) {
+        red_v[0][b] = v;
+        red_i[0][b] = idx;
       }
     }
   }
   __syncthreads();
 
-  // Publish this workgroup's candidates: wave w, slot t holds batch row w + 8 t.
-  float* part_v = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p.workspace) + LM_TICKET_BYTES);
+  // Publish this workgroup's candidates; the finalisation kernel that follows on the stream
+  // reduces them.
+  float* part_v = reinterpret_cast<float*>(p.workspace);
   int* part_i = reinterpret_cast<int*>(part_v + (size_t)n_tiles * LM_BATCH);
   if (tid < LM_BATCH) {
-    const int w = tid & 7, t = tid >> 3;  // batch row tid = w + 8 t
-    part_v[(size_t)tile * LM_BATCH + tid] = red_v[w][t];
-    part_i[(size_t)tile * LM_BATCH + tid] = red_i[w][t];
+    part_v[(size_t)tile * LM_BATCH + tid] = red_v[0][tid];
+    part_i[(size_t)tile * LM_BATCH + tid] = red_i[0][tid];
   }
-  __threadfence();
-  __syncthreads();
-  unsigned int* ticket = reinterpret_cast<unsigned int*>(p.workspace);
-  if (tid == 0) {
-    unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == (unsigned int)(n_tiles - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // Last workgroup: reduce every workgroup's candidates. Wave w handles batch rows w, w + 8, ...
-  for (int b = wave; b < nbatch; b += LM_WAVES) {
-    float v = -INFINITY;
-    int idx = 0x7fffffff;
-    for (int t = lane; t < n_tiles; t += 64) {
-      float tv = __hip_atomic_load(&part_v[(size_t)t * LM_BATCH + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int ti = __hip_atomic_load(&part_i[(size_t)t * LM_BATCH + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (better(tv, ti, v, idx)) {
-        v = tv;
-        idx = ti;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      float ov = __shfl_xor(v, off, 64);
-      int oi = __shfl_xor(idx, off, 64);
-      if (better(ov, oi, v, idx)) {
-        v = ov;
-        idx = oi;
-      }
-    }
-    if (lane == 0) {
-      if (idx == 0x7fffffff) idx = 0;  // every logit NaN: index 0, as the lowest index of -inf
-      p.argmax[b0 + b] = idx;
-      if (p.maxval != nullptr) p.maxval[b0 + b] = v;
-    }
-  }
-  if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-int lm_tiles(int V, int chunk, int* tiles_per_chunk) {
+// Reduces every workgroup's (max, lowest index) candidate of one batch row (one workgroup
+// per row): each thread loads its candidates with independent loads (one memory round trip),
+// then wave and workgroup reductions. Running as its own kernel after the logits kernel makes
+// the candidates visible across XCDs without device-scope fences in the streaming kernel.
+__global__ __launch_bounds__(LM_FIN_THREADS) void lm_head_argmax_kernel(LmHeadProblem p, int n_tiles, int b0) {
+  __shared__ float sv[LM_FIN_THREADS / 64];
+  __shared__ int si[LM_FIN_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const float* part_v = reinterpret_cast<const float*>(p.workspace);
+  const int* part_i = reinterpret_cast<const int*>(part_v + (size_t)n_tiles * LM_BATCH);
+  float v = -INFINITY;
+  int idx = 0x7fffffff;
+  for (int t = tid; t < n_tiles; t += LM_FIN_THREADS) {
+    const float tv = part_v[(size_t)t * LM_BATCH + b];
+    const int ti = part_i[(size_t)t * LM_BATCH + b];
+    if (better(tv, ti, v, idx)) {
+      v = tv;
+      idx = ti;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    float ov = __shfl_xor(v, off, 64);
+    int oi = __shfl_xor(idx, off, 64);
+    if (better(ov, oi, v, idx)) {
+      v = ov;
+      idx = oi;
+    }
+  }
+  if (lane == 0) {
+    sv[wave] = v;
+    si[wave] = idx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < LM_FIN_THREADS / 64; ++w)
+      if (better(sv[w], si[w], v, idx)) {
+        v = sv[w];
+        idx = si[w];
+      }
+    if (idx == 0x7fffffff) idx = 0;  // every logit NaN: index 0, as the lowest index of -inf
+    p.argmax[b0 + b] = idx;
+    if (p.maxval != nullptr) p.maxval[b0 + b] = v;
+  }
+}
+
+int lm_tiles(int V, int chunk, int rows, int* tiles_per_chunk) {
   const int n_chunks = (V + chunk - 1) / chunk;
-  const int per = (min(chunk, V) + LM_ROWS - 1) / LM_ROWS;
+  const int per = (min(chunk, V) + rows - 1) / rows;
   *tiles_per_chunk = per;
   const int last_rows = V - (n_chunks - 1) * chunk;
-  return (n_chunks - 1) * per + (last_rows + LM_ROWS - 1) / LM_ROWS;
+  return (n_chunks - 1) * per + (last_rows + rows - 1) / rows;
+}
+
+template <bool FP8, int S>
+void launch_shape(const LmHeadProblem& p, int b0, hipStream_t stream) {
+  constexpr LmShape sh = kLmShapes[S];
+  int per;
+  const int n_tiles = lm_tiles(p.V, p.chunk, sh.G * 16, &per);
+  hipLaunchKernelGGL((lm_head_kernel<FP8, sh.G, sh.W, sh.P>), dim3(n_tiles), dim3(sh.W * 64), 0, stream, p, per,
+                     n_tiles, b0);
+  hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(min(LM_BATCH, p.B - b0)), dim3(LM_FIN_THREADS), 0, stream, p,
+                     n_tiles, b0);
+}
+
+template <bool FP8>
+void launch_any(const LmHeadProblem& p, int shape, int b0, hipStream_t stream) {
+  switch (shape) {
+    case 1: launch_shape<FP8, 1>(p, b0, stream); break;
+    case 2: launch_shape<FP8, 2>(p, b0, stream); break;
+    case 3: launch_shape<FP8, 3>(p, b0, stream); break;
+    case 4: launch_shape<FP8, 4>(p, b0, stream); break;
+    case 5: launch_shape<FP8, 5>(p, b0, stream); break;
+    default: launch_shape<FP8, 0>(p, b0, stream); break;
+  }
 }
 
 }  // namespace
 
+int lm_head_shape_count() { return (int)(sizeof(kLmShapes) / sizeof(kLmShapes[0])); }
+
 size_t lm_head_workspace_bytes(int B, int V, int chunk) {
   (void)B;
-  int per;
-  const int n_tiles = lm_tiles(V, chunk, &per);
-  return LM_TICKET_BYTES + (size_t)n_tiles * LM_BATCH * (sizeof(float) + sizeof(int));
+  // sized for the launch shape with the most workgroups (16-row groups: the smallest tiles)
+  int per, n_tiles = 0;
+  for (const LmShape& sh : kLmShapes) n_tiles = max(n_tiles, lm_tiles(V, chunk, sh.G * 16, &per));
+  return (size_t)n_tiles * LM_BATCH * (sizeof(float) + sizeof(int));
 }
 
-hipError_t launch_lm_head(const LmHeadProblem& p, hipStream_t stream) {
-  int per;
-  const int n_tiles = lm_tiles(p.V, p.chunk, &per);
+hipError_t launch_lm_head(const LmHeadProblem& p, int shape, hipStream_t stream) {
+  if (shape < 0) shape = kLmDefaultShape;
+  if (shape >= lm_head_shape_count()) return hipErrorInvalidValue;
   for (int b0 = 0; b0 < p.B; b0 += LM_BATCH) {
     if (p.w_fp8)
-      hipLaunchKernelGGL(lm_head_kernel<true>, dim3(n_tiles), dim3(LM_THREADS), 0, stream, p, per, n_tiles, b0);
+      launch_any<true>(p, shape, b0, stream);
     else
-      hipLaunchKernelGGL(lm_head_kernel<false>, dim3(n_tiles), dim3(LM_THREADS), 0, stream, p, per, n_tiles, b0);
+      launch_any<false>(p, shape, b0, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

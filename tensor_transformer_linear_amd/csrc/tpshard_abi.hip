@@ -16,6 +16,7 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local int g_tile_override = tpk::TILE_AUTO;
 thread_local int g_path_override = tpk::GEMM_PATH_AUTO;
+thread_local int g_lm_shape_override = -1;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -199,15 +200,20 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
   return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_row_linear_partial launch");
 }
 
-TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K) {
+TP_API size_t tp_rmsnorm_workspace_min_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0) return 0;
   return align_up((size_t)M * sizeof(float), 256) + align_up((size_t)K * sizeof(uint16_t), 256);
 }
 
+TP_API size_t tp_rmsnorm_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return tp_rmsnorm_workspace_min_bytes(M, K) + align_up((size_t)M * (size_t)K * sizeof(uint16_t), 256);
+}
+
 TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
-                          const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
-                          int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                                 const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                                 int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   tpk::GemmProblem p;
   int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, TP_ACT_NONE, y, y_dtype,
                           layout, ldy, &p);
@@ -218,22 +224,27 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
     return fail(TP_ERR_UNSUPPORTED, "xnorm_out must be 16-byte aligned");
   if (workspace == nullptr && M > 0) return fail(TP_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const size_t need = tp_rmsnorm_workspace_bytes(M, K);
+  const size_t need = tp_rmsnorm_workspace_min_bytes(M, K);
   if (workspace_bytes < need)
-    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, at least %zu needed", workspace_bytes, need);
   if (M == 0) return ok();
 
-  float* r = static_cast<float*>(workspace);
-  uint16_t* t = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) + align_up((size_t)M * 4, 256));
+  // Workspace: r [M] f32 | t [K] bf16 | (fast path) the normalised rows [M, K] bf16.
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* r = reinterpret_cast<float*>(ws);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws + align_up((size_t)M * 4, 256));
+  uint16_t* rows = xnorm_out != nullptr ? static_cast<uint16_t*>(xnorm_out)
+                   : workspace_bytes >= tp_rmsnorm_workspace_bytes(M, K) ? reinterpret_cast<uint16_t*>(ws + need)
+                                                                         : nullptr;
   hipStream_t s = as_stream(stream);
   hipError_t e = tpk::launch_rmsnorm_rows(static_cast<const uint16_t*>(x), (int)M, (int)K,
-                                          static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr,
-                                          static_cast<uint16_t*>(xnorm_out), s);
+                                          static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr, rows, s);
   if (e != hipSuccess) return hip_status(e, "rmsnorm statistics launch");
-  if (xnorm_out != nullptr) {
-    // The normalised rows are materialised anyway: the GEMM reads them as a plain A.
-    p.A = static_cast<const uint16_t*>(xnorm_out);
+  if (rows != nullptr) {
+    // Normalised rows materialised: the GEMM reads them as a plain A (direct-to-LDS loop).
+    p.A = rows;
   } else {
+    // Fused: the GEMM normalises A while staging it (r per row, t per column).
     p.row_r = r;
     p.col_t = scale ? t : nullptr;
   }
@@ -294,7 +305,7 @@ TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t voc
   p.argmax = argmax_local;
   p.maxval = max_logit;
   p.workspace = workspace;
-  return hip_status(tpk::launch_lm_head(p, as_stream(stream)), "lm_head_shard_argmax launch");
+  return hip_status(tpk::launch_lm_head(p, g_lm_shape_override, as_stream(stream)), "lm_head_shard_argmax launch");
 }
 
 TP_API int tp_debug_set_gemm_tile(int tile) {
@@ -306,6 +317,12 @@ TP_API int tp_debug_set_gemm_tile(int tile) {
 TP_API int tp_debug_set_gemm_path(int path) {
   if (path < tpk::GEMM_PATH_AUTO || path > tpk::GEMM_PATH_DMA) return fail(TP_ERR_INVALID_ARG, "unknown path %d", path);
   g_path_override = path;
+  return ok();
+}
+
+TP_API int tp_debug_set_lm_head_shape(int shape) {
+  if (shape < -1 || shape >= tpk::lm_head_shape_count()) return fail(TP_ERR_INVALID_ARG, "unknown shape %d", shape);
+  g_lm_shape_override = shape;
   return ok();
 }
 

@@ -146,8 +146,10 @@ def test_rmsnorm_rejects(kw, status):
 
 
 def test_rmsnorm_workspace_size():
-    assert tt.tp_rmsnorm_workspace_bytes(32768, 8192) == 32768 * 4 + 8192 * 2
-    assert tt.tp_rmsnorm_workspace_bytes(3, 8) == 256 + 256
+    assert tt.tp_rmsnorm_workspace_min_bytes(32768, 8192) == 32768 * 4 + 8192 * 2
+    assert tt.tp_rmsnorm_workspace_min_bytes(3, 8) == 256 + 256
+    assert tt.tp_rmsnorm_workspace_bytes(32768, 8192) == 32768 * 4 + 8192 * 2 + 32768 * 8192 * 2
+    assert tt.tp_rmsnorm_workspace_bytes(3, 8) == 256 + 256 + 256
 
 
 def lm(**kw):
