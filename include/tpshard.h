@@ -234,8 +234,12 @@ TP_API const char* tp_version(void);
  *                          (needs K % 32 == 0 and no RMSNorm transform; a call that cannot
  *                          use it returns TP_ERR_HIP).
  * tp_debug_set_lm_head_shape forces the LM head's launch shape on this thread: -1 default,
- *                          0..5 (16-row weight groups per workgroup, waves, K steps per load
- *                          batch) = (4,8,8) (2,8,8) (4,4,8) (2,4,8) (4,8,4) (1,8,8).
+ *                          0..9: register-streaming kernel (16-row weight groups per
+ *                          workgroup, waves, K steps per load batch, workgroups splitting
+ *                          K) = (4,8,8,1) (2,8,8,1) (4,4,8,1) (2,4,8,1) (4,8,4,1) (1,8,8,1)
+ *                          (8,8,4,2) (8,4,4,2); 8, 9 = direct-to-LDS kernel (64 rows, 4
+ *                          waves, LDS ring of 64- or 128-byte row stages; a bf16 K that is
+ *                          not a multiple of 32 or 64 falls back to shape 4).
  * tp_debug_gemm_pick_tile  the automatic choice for an M x N x K problem (-1 if invalid).
  */
 TP_API int tp_debug_set_gemm_tile(int tile);

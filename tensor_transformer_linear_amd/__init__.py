@@ -218,7 +218,8 @@ def set_lm_head_shape(shape: int) -> None:
     _check(lib().tp_debug_set_lm_head_shape(shape))
 
 
-LM_HEAD_SHAPES = {0: (4, 8, 8), 1: (2, 8, 8), 2: (4, 4, 8), 3: (2, 4, 8), 4: (4, 8, 4), 5: (1, 8, 8)}
+LM_HEAD_SHAPES = {0: (4, 8, 8, 1), 1: (2, 8, 8, 1), 2: (4, 4, 8, 1), 3: (2, 4, 8, 1), 4: (4, 8, 4, 1),
+                  5: (1, 8, 8, 1), 6: (8, 8, 4, 2), 7: (8, 4, 4, 2), 8: ("lds-ring", 64), 9: ("lds-ring", 128)}
 
 
 def gemm_pick_tile(M: int, N: int, K: int) -> int:

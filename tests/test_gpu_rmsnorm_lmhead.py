@@ -151,3 +151,19 @@ def test_lm_head_every_launch_shape(shape, fp8):
         assert argmax_ok(idx.cpu().numpy(), ref) == []
     finally:
         tt.set_lm_head_shape(-1)
+
+
+@pytest.mark.parametrize("shape", [8, 9])
+@pytest.mark.parametrize("B,K", [(40, 256), (3, 96), (9, 200)])
+def test_lm_head_lds_ring_batch_passes_and_ragged_k(shape, B, K):
+    """The LDS-ring kernels over two 32-row batch passes, and with a bf16 K that their stage
+    width does not divide (96 for 64-wide stages, 200 for both), where the launcher falls back
+    to the register-streaming kernel."""
+    tt.set_lm_head_shape(shape)
+    try:
+        for fp8 in ([False, True] if K % 128 == 0 else [False]):
+            lg, idx, mx, ref = _lm_case(B, K, 2 * 1000 + 37, 2, 1, 500, 90 + shape, fp8)
+            assert_close(host_f32(lg), ref, what=f"shape {shape} fp8 {fp8}")
+            assert argmax_ok(idx.cpu().numpy(), ref) == []
+    finally:
+        tt.set_lm_head_shape(-1)
