@@ -5,14 +5,16 @@
 // column- or row-parallel linear ([deepspeed] SubParamLinearLayer.forward,
 // [nanotron] "MLP Module").
 //
-// Structure: one workgroup owns a BM x BN output tile and walks K in steps of
-// 64. Each step's A and B slabs go global -> registers -> LDS (two LDS stages:
-// the loads of step k+1 are in flight while step k's MFMAs run). Each wave owns
-// a WM x WN sub-tile made of 32x32 blocks, computed with
-// v_mfma_f32_32x32x16_bf16 from 16-byte LDS reads. LDS rows are 128 bytes
-// (64 bf16 of K); the 16-byte chunk index is XORed with bits 1..3 of the row so
-// that the sixteen rows one ds_read_b128 phase touches hit distinct banks.
-// Optionally the A slab is RMS-normalised on its way into LDS.
+// A workgroup owns a BM x BN output tile and walks K; each wave owns a WM x WN
+// sub-tile of 32x32 blocks computed with v_mfma_f32_32x32x16_bf16 from 16-byte
+// LDS reads. Two main loops feed the LDS:
+// * direct-to-LDS (the default when K % 32 == 0 and A needs no transform): each
+//   32-wide K step goes global -> LDS with global_load_lds_dwordx4 into a ring of
+//   stages, several in flight, with the operand fragments double-buffered in
+//   registers so the LDS reads of one half-step overlap the MFMAs of the other;
+// * register staging (any K % 8 == 0, and the fused RMSNorm): 64-wide K steps
+//   go global -> registers -> LDS through two stages; the A slab can be
+//   RMS-normalised on its way into LDS.
 // The output stage adds the bias, applies GELU, rounds once and stores bf16
 // or f32 at the (possibly remapped) output column, or adds into f32.
 #include "common.h"
@@ -302,7 +304,12 @@ __device__ __forceinline__ void dma_load16(const uint16_t* g, lds_byte* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+// 4 bytes per lane from global memory into LDS at lds + 4 * lane: pulls the line into L2.
+__device__ __forceinline__ void dma_touch4(const uint16_t* g, lds_byte* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int PFD>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                             int group_m) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -317,7 +324,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be whole 32x32 blocks");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "tile rows must fill DMA blocks");
   constexpr int EPI = WAVES_M * 32 * (BN + 4) * 4;
-  constexpr int SMEM = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
+  constexpr int RING = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
+  // PFD > 0: every stage's DMA is followed by one 4-byte-per-lane load that pulls the 128-byte
+  // lines of stage + PFD into L2 (half of the tile's rows per stage, alternating, so every line
+  // of a stage pair is touched once); its LDS writes go to a scratch slot nobody reads.
+  constexpr int PF_OPS = PFD > 0 ? 1 : 0;
+  constexpr int SMEM = RING + (PFD > 0 ? 256 : 0);
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -348,11 +360,24 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     }
     dst[b] = blk * 1024;
   }
+  // L2 prefetch rows of this thread: row tid (even stages) or tid + NT (odd stages) of the
+  // tile's BM + BN rows, wrapped, clamped like the DMA rows.
+  const uint16_t* pf_row[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid + h * NT) % (BM + BN);
+    pf_row[h] = r < BM ? p.A + (int64_t)min(m0 + r, M - 1) * p.lda : p.B + (int64_t)min(n0 + r - BM, N - 1) * p.ldb;
+  }
   auto issue = [&](int kt) {
+    const int kp = kt + PFD;
     kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
     lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
 #pragma unroll
     for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + kt * DBK, base + dst[b]);
+    if constexpr (PFD > 0) {
+      const int ke = min(kp, nk - 1) & ~1;  // even stage: the start of a 128-byte line
+      dma_touch4(pf_row[kp & 1] + ke * DBK, (lds_byte*)smem + RING);
+    }
   };
 
   f32x16_t acc[FM][FN];
@@ -361,54 +386,83 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   });
   const int a_row0 = wm * WM + (lane & 31), b_row0 = wn * WN + (lane & 31);
   const int khalf = lane >> 5;
-  auto compute = [&](int stage) {
+  // Operand fragments of one 16-wide half of a K step: lane l holds row l % 32 of each
+  // 32-row block and K values 8 (l / 32) .. +8 of the half.
+  struct Frag {
+    bf16x8_t a[FM], b[FN];
+  };
+  auto read = [&](Frag& f, int stage, int half) {
     const unsigned char* sa = smem + stage * STAGE;
     const unsigned char* sb = sa + BM * DROW;
-    static_for<DBK / 16>([&](auto kk) {
-      bf16x8_t af[FM], bfr[FN];
-      static_for<FM>([&](auto i) {
-        af[i] = __builtin_bit_cast(bf16x8_t,
-                                   *reinterpret_cast<const u32x4_t*>(sa + dma_off(a_row0 + i * 32, kk * 2 + khalf)));
-      });
+    static_for<FM>([&](auto i) {
+      f.a[i] = __builtin_bit_cast(bf16x8_t,
+                                  *reinterpret_cast<const u32x4_t*>(sa + dma_off(a_row0 + i * 32, half * 2 + khalf)));
+    });
+    static_for<FN>([&](auto j) {
+      f.b[j] = __builtin_bit_cast(bf16x8_t,
+                                  *reinterpret_cast<const u32x4_t*>(sb + dma_off(b_row0 + j * 32, half * 2 + khalf)));
+    });
+  };
+  auto mma = [&](const Frag& f) {
+    static_for<FM>([&](auto i) {
       static_for<FN>([&](auto j) {
-        bfr[j] = __builtin_bit_cast(bf16x8_t,
-                                    *reinterpret_cast<const u32x4_t*>(sb + dma_off(b_row0 + j * 32, kk * 2 + khalf)));
-      });
-      static_for<FM>([&](auto i) {
-        static_for<FN>([&](auto j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        });
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
       });
     });
   };
-
-  // Prologue: stages 0 .. STAGES-2 in flight. Step kt: wait until only the STAGES-2 newer
-  // stages' loads of this wave are outstanding, barrier (all waves' loads of stage kt have
-  // landed, and every wave finished step kt-1, whose buffer the next issue overwrites),
-  // issue step kt + STAGES - 1, multiply step kt.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // s_waitcnt with vmcnt = (STAGES - 2) * BLK_PER_WAVE, expcnt and lgkmcnt left open
-    // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-    constexpr int VM = (STAGES - 2) * BLK_PER_WAVE;
-    static_assert(VM < 64, "vmcnt immediate is six bits");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
-    // Workgroup barrier without a memory fence: a fence would make the compiler drain every
-    // outstanding load (vmcnt 0) and serialise the stages. The wait above already covers
-    // this wave's loads of stage kt; the empty asm statements keep the compiler from moving
-    // LDS accesses across the barrier.
+  // s_waitcnt vmcnt(VM) with expcnt and lgkmcnt left open (gfx9 encoding: vmcnt[3:0] |
+  // expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]), then a workgroup barrier without a
+  // memory fence: a fence would make the compiler drain every outstanding load (vmcnt 0)
+  // and serialise the stages. The empty asm statements keep the compiler from moving LDS
+  // accesses across the barrier; the scheduling barriers keep the MFMAs on their side.
+  auto wait_barrier = [&](auto vm, auto lgkm) {
+    constexpr int VM = decltype(vm)::value, LGKM = decltype(lgkm)::value;
+    static_assert(VM >= 0 && VM < 64, "vmcnt immediate is six bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Software pipeline over K steps, two register sets of fragments. Step kt enters with the
+  // first half of stage kt in f0; it reads the second half into f1 and multiplies f0 (the
+  // MFMAs cover the LDS latency); waits until stage kt + 1 has landed in every wave (at most
+  // the STAGES - 3 newer stages of this wave outstanding) behind a barrier, which also proves
+  // every wave is done with stage kt - 1, whose slot the next DMA overwrites; issues stage
+  // kt + STAGES - 1; reads the first half of stage kt + 1 into f0 and multiplies f1.
+  static_assert(STAGES >= 3, "the pipeline reads one stage ahead");
+  constexpr int OPS = BLK_PER_WAVE + PF_OPS;  // loads per stage per wave, the prefetch last
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  wait_barrier(std::integral_constant<int, (STAGES - 2) * OPS + PF_OPS>{}, std::integral_constant<int, 15>{});
+  // Scheduling barriers pin each phase: left alone, the scheduler sinks every read to just
+  // before the MFMAs that consume it, which exposes the LDS latency again. Each multiply
+  // phase ends with lgkmcnt(0): the reads issued before it have long completed, and with
+  // only one set of reads ever outstanding the compiler needs no wait of its own before the
+  // next multiply (with two sets, 16 reads, it falls back to draining both).
+  Frag f0, f1;
+  read(f0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // both edges into the loop arrive with no reads pending
+  for (int kt = 0; kt < nk; ++kt) {
+    read(f1, kt % STAGES, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    wait_barrier(std::integral_constant<int, (STAGES - 3) * OPS + PF_OPS>{}, std::integral_constant<int, 0>{});
     issue(kt + STAGES - 1);
-    compute(kt % STAGES);
+    read(f0, (kt + 1) % STAGES, 0);  // past the last step: a slot of clamped data, never multiplied
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int PFD = 0>
 hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nb = tiles_m * tiles_n;
@@ -417,7 +471,7 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
   if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER)
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>), grid, block, 0, stream, p, tiles_m,
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, PFD>), grid, block, 0, stream, p, tiles_m,
                        tiles_n, group_m);
   else if (p.row_r != nullptr)
     hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
@@ -433,7 +487,7 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 512) return TILE_256x256;
+  if (t256 >= 192) return TILE_256x256;  // the 8-wave 256x256 tile wins even with a partial last wave
   if (N % 224 == 0 && (long long)((M + 255) / 256) * (N / 224) >= 256) return TILE_256x224;
   const long long t256x128 = (long long)((M + 255) / 256) * ((N + 127) / 128);
   if (t256x128 >= 256) return TILE_256x128;
@@ -446,11 +500,11 @@ int gemm_pick_tile(int M, int N, int K) {
 hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream) {
   if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.N, p.K);
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, 2, 2, 4>(p, path, stream);
-    case TILE_256x128: return launch_tile<256, 128, 2, 2, 5>(p, path, stream);
-    case TILE_128x128: return launch_tile<128, 128, 2, 2, 4>(p, path, stream);
-    case TILE_128x256: return launch_tile<128, 256, 2, 2, 5>(p, path, stream);
-    case TILE_256x224: return launch_tile<256, 224, 4, 1, 4>(p, path, stream);
+    case TILE_256x256: return launch_tile<256, 256, 2, 4, 4>(p, path, stream);  // 8 waves: two per SIMD
+    case TILE_256x128: return launch_tile<256, 128, 2, 2, 6>(p, path, stream);
+    case TILE_128x128: return launch_tile<128, 128, 2, 2, 5>(p, path, stream);
+    case TILE_128x256: return launch_tile<128, 256, 2, 2, 6>(p, path, stream);
+    case TILE_256x224: return launch_tile<256, 224, 4, 1, 5>(p, path, stream);
     case TILE_128x64: return launch_tile<128, 64, 2, 2, 4>(p, path, stream);
     case TILE_64x64: return launch_tile<64, 64, 2, 2, 4>(p, path, stream);
     default: return hipErrorInvalidValue;
