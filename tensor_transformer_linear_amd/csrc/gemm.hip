@@ -304,12 +304,7 @@ __device__ __forceinline__ void dma_load16(const uint16_t* g, lds_byte* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-// 4 bytes per lane from global memory into LDS at lds + 4 * lane: pulls the line into L2.
-__device__ __forceinline__ void dma_touch4(const uint16_t* g, lds_byte* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
-}
-
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int PFD>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                             int group_m) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -324,12 +319,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   static_assert(FM * 32 == WM && FN * 32 == WN, "wave tile must be whole 32x32 blocks");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "tile rows must fill DMA blocks");
   constexpr int EPI = WAVES_M * 32 * (BN + 4) * 4;
-  constexpr int RING = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
-  // PFD > 0: every stage's DMA is followed by one 4-byte-per-lane load that pulls the 128-byte
-  // lines of stage + PFD into L2 (half of the tile's rows per stage, alternating, so every line
-  // of a stage pair is touched once); its LDS writes go to a scratch slot nobody reads.
-  constexpr int PF_OPS = PFD > 0 ? 1 : 0;
-  constexpr int SMEM = RING + (PFD > 0 ? 256 : 0);
+  constexpr int SMEM = STAGES * STAGE > EPI ? STAGES * STAGE : EPI;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -360,24 +350,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     }
     dst[b] = blk * 1024;
   }
-  // L2 prefetch rows of this thread: row tid (even stages) or tid + NT (odd stages) of the
-  // tile's BM + BN rows, wrapped, clamped like the DMA rows.
-  const uint16_t* pf_row[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = (tid + h * NT) % (BM + BN);
-    pf_row[h] = r < BM ? p.A + (int64_t)min(m0 + r, M - 1) * p.lda : p.B + (int64_t)min(n0 + r - BM, N - 1) * p.ldb;
-  }
   auto issue = [&](int kt) {
-    const int kp = kt + PFD;
     kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
     lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
 #pragma unroll
     for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + kt * DBK, base + dst[b]);
-    if constexpr (PFD > 0) {
-      const int ke = min(kp, nk - 1) & ~1;  // even stage: the start of a 128-byte line
-      dma_touch4(pf_row[kp & 1] + ke * DBK, (lds_byte*)smem + RING);
-    }
   };
 
   f32x16_t acc[FM][FN];
@@ -433,10 +410,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   // every wave is done with stage kt - 1, whose slot the next DMA overwrites; issues stage
   // kt + STAGES - 1; reads the first half of stage kt + 1 into f0 and multiplies f1.
   static_assert(STAGES >= 3, "the pipeline reads one stage ahead");
-  constexpr int OPS = BLK_PER_WAVE + PF_OPS;  // loads per stage per wave, the prefetch last
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
-  wait_barrier(std::integral_constant<int, (STAGES - 2) * OPS + PF_OPS>{}, std::integral_constant<int, 15>{});
+  wait_barrier(std::integral_constant<int, (STAGES - 2) * BLK_PER_WAVE>{}, std::integral_constant<int, 15>{});
   // Scheduling barriers pin each phase: left alone, the scheduler sinks every read to just
   // before the MFMAs that consume it, which exposes the LDS latency again. Each multiply
   // phase ends with lgkmcnt(0): the reads issued before it have long completed, and with
@@ -449,7 +425,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     read(f1, kt % STAGES, 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
-    wait_barrier(std::integral_constant<int, (STAGES - 3) * OPS + PF_OPS>{}, std::integral_constant<int, 0>{});
+    wait_barrier(std::integral_constant<int, (STAGES - 3) * BLK_PER_WAVE>{}, std::integral_constant<int, 0>{});
     issue(kt + STAGES - 1);
     read(f0, (kt + 1) % STAGES, 0);  // past the last step: a slot of clamped data, never multiplied
     __builtin_amdgcn_sched_barrier(0);
@@ -462,7 +438,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int PFD = 0>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nb = tiles_m * tiles_n;
@@ -471,7 +447,7 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
   if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER)
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, PFD>), grid, block, 0, stream, p, tiles_m,
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>), grid, block, 0, stream, p, tiles_m,
                        tiles_n, group_m);
   else if (p.row_r != nullptr)
     hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
