@@ -10,8 +10,11 @@
 // LDS reads. Two main loops feed the LDS:
 // * direct-to-LDS (the default when K % 32 == 0 and A needs no transform): each
 //   32-wide K step goes global -> LDS with global_load_lds_dwordx4 into a ring of
-//   stages, several in flight, with the operand fragments double-buffered in
-//   registers so the LDS reads of one half-step overlap the MFMAs of the other;
+//   stages, several in flight. The 256x256 tile runs eight waves in two groups
+//   that ping-pong (one group multiplies while the other reads its next
+//   fragments and issues the next loads); other tiles double-buffer the operand
+//   fragments in registers so the LDS reads of one half-step overlap the MFMAs
+//   of the other;
 // * register staging (any K % 8 == 0, and the fused RMSNorm): 64-wide K steps
 //   go global -> registers -> LDS through two stages; the A slab can be
 //   RMS-normalised on its way into LDS.
@@ -304,7 +307,12 @@ __device__ __forceinline__ void dma_load16(const uint16_t* g, lds_byte* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+// SCHED selects the main-loop schedule: 0 = every wave multiplies while its own next reads fly
+// (fragments double-buffered in registers); 1 = ping-pong between two groups of four waves (one
+// wave per SIMD each, eight waves per workgroup): one group multiplies while the other reads
+// its next fragments from LDS and issues the next global loads, and the roles swap at every
+// barrier, so each SIMD always has a wave issuing MFMAs.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                             int group_m) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -403,6 +411,48 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  if constexpr (SCHED == 1) {
+    static_assert(WAVES_M == 2 && NWAVE == 8, "ping-pong needs two groups of four waves");
+    // Group g = wm: waves 0-3 and 4-7, one wave of each group per SIMD. Group 1 runs one phase
+    // behind group 0. Memory phase k: read both halves of stage k, issue stage k + STAGES - 1
+    // into the slot of stage k - 1, then wait until this wave's loads of stage k + 1 have
+    // landed (at most the STAGES - 2 newer stages outstanding) and its reads are done, and
+    // meet the other group at the barrier. Compute phase k: 16 MFMAs, barrier. A group reads
+    // stage k only after both groups waited for their loads of it (its own wait one memory
+    // phase earlier, the other group's before the barrier between them), and a slot is
+    // overwritten two phases after both groups finished reading it. Every wave executes the
+    // same number of barriers: the prologue's, 2 per K step, and one extra (group 1 at the
+    // start, group 0 at the end).
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s);
+    wait_barrier(std::integral_constant<int, (STAGES - 2) * BLK_PER_WAVE>{}, std::integral_constant<int, 15>{});
+    if (wm == 1) {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    Frag f0, f1;
+    for (int kt = 0; kt < nk; ++kt) {
+      read(f0, kt % STAGES, 0);
+      read(f1, kt % STAGES, 1);
+      issue(kt + STAGES - 1);
+      wait_barrier(std::integral_constant<int, (STAGES - 2) * BLK_PER_WAVE>{}, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_s_setprio(1);  // the multiplying wave first: the other group only issues memory work
+      mma(f0);
+      mma(f1);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (wm == 0) {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+    return;
+  }
+
   // Software pipeline over K steps, two register sets of fragments. Step kt enters with the
   // first half of stage kt in f0; it reads the second half into f1 and multiplies f0 (the
   // MFMAs cover the LDS latency); waits until stage kt + 1 has landed in every wave (at most
@@ -438,16 +488,16 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED = 0>
 hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int nb = tiles_m * tiles_n;
-  const int group_m = tiles_m < 8 ? tiles_m : 8;
+  const int group_m = tiles_m < 4 ? tiles_m : 4;  // 4 M-tiles per group: measured best for L2 reuse
   dim3 grid(nb), block(WAVES_M * WAVES_N * 64);
   const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
   if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER)
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES>), grid, block, 0, stream, p, tiles_m,
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, SCHED>), grid, block, 0, stream, p, tiles_m,
                        tiles_n, group_m);
   else if (p.row_r != nullptr)
     hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
@@ -476,7 +526,7 @@ int gemm_pick_tile(int M, int N, int K) {
 hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream) {
   if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.N, p.K);
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, 2, 4, 4>(p, path, stream);  // 8 waves: two per SIMD
+    case TILE_256x256: return launch_tile<256, 256, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_256x128: return launch_tile<256, 128, 2, 2, 6>(p, path, stream);
     case TILE_128x128: return launch_tile<128, 128, 2, 2, 5>(p, path, stream);
     case TILE_128x256: return launch_tile<128, 256, 2, 2, 6>(p, path, stream);

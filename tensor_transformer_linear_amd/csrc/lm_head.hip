@@ -312,7 +312,10 @@ constexpr int LMD_ROWS = 64;
 constexpr int LMD_THREADS = 256;
 
 typedef __attribute__((address_space(3))) unsigned char lmd_lds;
-__device__ __forceinline__ void lmd_dma16(const void* g, lmd_lds* lds) { __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0); }
+// cache-policy bits of the global_load_lds aux operand
+constexpr int LMD_POLICY_DEFAULT = 0;
+template <int POLICY>
+__device__ __forceinline__ void lmd_dma16(const void* g, lmd_lds* lds) { __builtin_amdgcn_global_load_lds(g, lds, 16, 0, POLICY); }
 __device__ __forceinline__ void lmd_dma4(const void* g, lmd_lds* lds) { __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0); }
 
 // byte offset of logical chunk c of row `row` in an LDS array of ROWB-byte rows
@@ -327,13 +330,15 @@ template <bool FP8, int RB>
 struct LmdStage {
   static constexpr int KW = FP8 ? RB : RB / 2;  // K values per stage
   static constexpr int XB = KW * 2;             // x bytes per row per stage
-  static constexpr int NWB = LMD_ROWS * RB / 1024;        // weight DMA blocks
+  static constexpr int NWB = LMD_ROWS * RB / 1024;        // weight DMA blocks (a multiple of 4)
   static constexpr int NXB = LM_BATCH * XB / 1024;        // x DMA blocks
-  static constexpr int BLK_PER_WAVE = (NWB + NXB + 3) / 4;
+  static constexpr int WPW = NWB / 4;                     // weight blocks per wave
+  static constexpr int XPW = (NXB + 3) / 4;               // x blocks per wave (padded)
   static constexpr int X_OFF = NWB * 1024;
-  static constexpr int S_OFF = 4 * BLK_PER_WAVE * 1024;  // E4M3 scales after the (padded) blocks
+  static constexpr int S_OFF = X_OFF + 4 * XPW * 1024;    // E4M3 scales after x and its padding
   static constexpr int BYTES = S_OFF + (FP8 ? 1024 : 0);
-  static constexpr int OPS = BLK_PER_WAVE + (FP8 ? 1 : 0);  // loads per wave per stage
+  static constexpr int OPS = WPW + XPW + (FP8 ? 1 : 0);   // loads per wave per stage
+  static_assert(NWB % 4 == 0, "weight blocks split evenly over the waves");
 };
 
 template <bool FP8, int RB, int STAGES>
@@ -352,42 +357,44 @@ __global__ __launch_bounds__(LMD_THREADS) void lm_head_dma_kernel(LmHeadProblem 
   const int nst = K / KW;
   const int nblk = K / 128;
 
-  // This lane's DMA sources: block b of the wave is stage block wave + 4 b (weight blocks,
-  // then x blocks, then padding that repeats block 0). Rows past the tile or the batch read
-  // a clamped row: they only feed outputs that are never stored.
-  const unsigned char* src[SG::BLK_PER_WAVE];
-  int dst[SG::BLK_PER_WAVE];
-  int adv[SG::BLK_PER_WAVE];  // source bytes per stage
+  // This lane's DMA sources: weight block wave + 4 b (b < WPW) and x block wave + 4 b (b < XPW;
+  // x blocks past NXB repeat x block 0 into padding). Rows past the tile or the batch read a
+  // clamped row: they only feed outputs that are never stored.
+  const unsigned char* wsrc[SG::WPW];
+  const unsigned char* xsrc[SG::XPW];
 #pragma unroll
-  for (int b = 0; b < SG::BLK_PER_WAVE; ++b) {
-    int blk = wave + 4 * b;
-    dst[b] = blk * 1024;
-    if (blk >= SG::NWB + SG::NXB) blk = 0;
-    if (blk < SG::NWB) {
-      constexpr int RPB = 1024 / RB;  // rows per block
-      const int row = blk * RPB + lane / (RB / 16);
-      const int c = (lane % (RB / 16)) ^ ((row / (16 / (RB / 16))) & (RB / 16 - 1));
-      const int grow = row0 + (row < nrows ? row : 0);
-      src[b] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)grow * (FP8 ? K : 2 * K) + c * 16;
-      adv[b] = RB;
-    } else {
-      constexpr int RPB = 1024 / XB;
-      const int xr = (blk - SG::NWB) * RPB + lane / (XB / 16);
-      const int c = (lane % (XB / 16)) ^ ((xr / (16 / (XB / 16))) & (XB / 16 - 1));
-      src[b] = reinterpret_cast<const unsigned char*>(p.x + (int64_t)(b0 + (xr < nbatch ? xr : 0)) * K) + c * 16;
-      adv[b] = XB;
-    }
+  for (int b = 0; b < SG::WPW; ++b) {
+    const int blk = wave + 4 * b;
+    constexpr int RPB = 1024 / RB;  // rows per block
+    const int row = blk * RPB + lane / (RB / 16);
+    const int c = (lane % (RB / 16)) ^ ((row / (16 / (RB / 16))) & (RB / 16 - 1));
+    const int grow = row0 + (row < nrows ? row : 0);
+    wsrc[b] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)grow * (FP8 ? K : 2 * K) + c * 16;
+  }
+#pragma unroll
+  for (int b = 0; b < SG::XPW; ++b) {
+    const int blk = (wave + 4 * b) < SG::NXB ? wave + 4 * b : 0;
+    constexpr int RPB = 1024 / XB;
+    const int xr = blk * RPB + lane / (XB / 16);
+    const int c = (lane % (XB / 16)) ^ ((xr / (16 / (XB / 16))) & (XB / 16 - 1));
+    xsrc[b] = reinterpret_cast<const unsigned char*>(p.x + (int64_t)(b0 + (xr < nbatch ? xr : 0)) * K) + c * 16;
   }
   const float* ssrc = nullptr;
   if constexpr (FP8) {
     const int row = wave * 16 + (lane & 15);
     ssrc = p.wscale + (int64_t)(row0 + (row < nrows ? row : 0)) * nblk;
   }
+  // Both streams use the default cache policy: the non-temporal policy on the weight blocks
+  // (read once) measured slower here than the default.
   auto issue = [&](int st) {
     st = st < nst ? st : nst - 1;  // clamped: the loop issues unconditionally
     lmd_lds* base = (lmd_lds*)ring + (st % STAGES) * STAGE;
 #pragma unroll
-    for (int b = 0; b < SG::BLK_PER_WAVE; ++b) lmd_dma16(src[b] + (size_t)st * adv[b], base + dst[b]);
+    for (int b = 0; b < SG::WPW; ++b)
+      lmd_dma16<LMD_POLICY_DEFAULT>(wsrc[b] + (size_t)st * RB, base + (wave + 4 * b) * 1024);
+#pragma unroll
+    for (int b = 0; b < SG::XPW; ++b)
+      lmd_dma16<LMD_POLICY_DEFAULT>(xsrc[b] + (size_t)st * XB, base + SG::X_OFF + (wave + 4 * b) * 1024);
     if constexpr (FP8) lmd_dma4(ssrc + st * KW / 128, base + SG::S_OFF + wave * 256);
   };
 
