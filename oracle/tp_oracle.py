@@ -419,3 +419,98 @@ def global_argmax(per_rank):
             best_v = np.where(better, mx, best_v)
             best_i = np.where(better, g, best_i)
     return best_i, best_v
+
+
+# --------------------------------------------------------------------------------------
+# F1 - fp8 prefill column linear  [palm] transformer_layer_weight_gathered (QuantizedLayer)
+# --------------------------------------------------------------------------------------
+#
+# [palm] multiplies the normalised activations by the quantised ``q_wi`` weights and then
+# applies the per-output-channel ``q_wi_scale`` to the matmul result before casting it to
+# the intermediate dtype.  Reading taken for a product on fp8 matrix cores: the weights
+# are stored as E4M3 codes with one float32 scale per output channel (a storage format,
+# produced by the input generator), and the activations are quantised per row (one float32
+# scale per token) by the method itself, as defined here; both scales and the bias are
+# applied to the exact product.
+
+E4M3_MAX = 448.0
+
+# finite non-negative E4M3 values in increasing order, and their codes
+_E4M3_POS_CODES = np.array([c for c in range(0x7F)], dtype=np.uint8)  # 0x00 .. 0x7E
+_E4M3_POS_VALS = _E4M3[:0x7F]
+
+
+def e4m3_encode(v32: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of float32 values: ties to the code with the even mantissa, and
+    magnitudes of 448 or more saturate to 448 (the format has no infinity).
+
+    Follows the OCP 8-bit definition: every finite E4M3 value is a candidate; the nearest one
+    wins; on an exact tie the candidate whose 3-bit mantissa is even (code LSB 0) wins, which
+    is round-to-nearest-even on the significand.  NaN inputs are not defined here.
+    """
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    mag = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS_VALS, mag, side="left")  # first value >= mag
+    hi = np.minimum(hi, len(_E4M3_POS_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - _E4M3_POS_VALS[lo]
+    d_hi = _E4M3_POS_VALS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((_E4M3_POS_CODES[hi] & 1) == 0))
+    code = np.where(pick_hi, _E4M3_POS_CODES[hi], _E4M3_POS_CODES[lo]).astype(np.uint8)
+    code = np.where(mag == _E4M3_POS_VALS[hi], _E4M3_POS_CODES[hi], code).astype(np.uint8)
+    return np.where(v < 0, code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x_bits):
+    """Per-row (per-token) E4M3 quantisation of bf16 activations.
+
+    Row m: ``s[m] = f32(amax_k |x[m,k]| / 448)`` (1 for an all-zero row), then
+    ``q[m,k] = e4m3(f32(x[m,k] / s[m]))`` with both divisions rounded to float32 once
+    (nearest even).  The row's largest magnitude maps to 448 up to that rounding; larger
+    quotients saturate.  Returns ``(codes uint8 [M,K], scales float32 [M])``.
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    s = (amax.astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    q = e4m3_encode((x / s[:, None]).astype(np.float32))
+    return q, s
+
+
+def column_linear_fp8(xq, x_scale, wq_shard, w_scale_shard, bias_shard_bits, subparam_sizes, tp_size, rank,
+                      act=ACT_NONE, out_dtype=OUT_BF16, layout=LAYOUT_LOCAL, n_logical=None):
+    """One rank's column-parallel linear on E4M3 activations and weights.
+
+    ``acc = sum_k dec(xq[m,k]) dec(wq[j,k])`` (exact in float64: every product of two E4M3
+    values is exact), ``v = x_scale[m] * w_scale[j] * acc + b[j]`` (float64), then as
+    ``column_linear``: ``a = f32(v)``, GELU on ``a`` if asked, one rounding to the output
+    type, LOCAL or LOGICAL placement of the shard's columns.
+    """
+    x = e4m3_to_f64(xq)
+    w = e4m3_to_f64(wq_shard)
+    width, loff, lcl, total = shard_widths(subparam_sizes, tp_size, rank)
+    if w.shape[0] != total:
+        raise ValueError(f"weight shard has {w.shape[0]} rows, shard total is {total}")
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x and weight K differ")
+    acc = x @ w.T
+    v = np.asarray(x_scale, np.float64)[:, None] * np.asarray(w_scale_shard, np.float64)[None, :] * acc
+    if bias_shard_bits is not None:
+        b = bf16_to_f64(bias_shard_bits)
+        if b.shape != (total,):
+            raise ValueError(f"bias shard has {b.size} entries, expected {total}")
+        v = v + b[None, :]
+    a = f32(v)
+    if act == ACT_GELU:
+        a = f32(gelu_erf(a))
+    y = bf16_round(a) if out_dtype == OUT_BF16 else a
+    if layout == LAYOUT_LOCAL:
+        return y
+    if n_logical is None:
+        n_logical = sum(int(s) for s in subparam_sizes)
+    out = np.zeros((y.shape[0], n_logical), dtype=y.dtype)
+    mask = np.zeros(n_logical, dtype=bool)
+    for wd, lo, lc in zip(width, loff, lcl):
+        out[:, lo:lo + wd] = y[:, lc:lc + wd]
+        mask[lo:lo + wd] = True
+    return out, mask

@@ -111,25 +111,32 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     return (code | (neg.astype(np.uint8) << 7)).astype(np.uint8)
 
 
-def quantize_e4m3_blocks(w_bits: np.ndarray, chunk_rows: int = 2048):
-    """Per-row, per-128-K-block E4M3 storage of a bf16 weight ``[rows, K]``.
+def quantize_e4m3_blocks(w_bits: np.ndarray, chunk_rows: int = 2048, block: int = FP8_BLOCK):
+    """Per-row, per-``block``-K-block E4M3 storage of a bf16 weight ``[rows, K]``.
 
-    Returns ``(codes uint8 [rows, K], scales float32 [rows, K // 128])``.  Rows are
+    Returns ``(codes uint8 [rows, K], scales float32 [rows, K // block])``.  Rows are
     processed in blocks to bound the temporaries; each row's result is independent.
     """
     rows, k = w_bits.shape
-    if k % FP8_BLOCK:
-        raise ValueError(f"K={k} must be a multiple of {FP8_BLOCK}")
+    if k % block:
+        raise ValueError(f"K={k} must be a multiple of {block}")
     q = np.empty((rows, k), dtype=np.uint8)
-    scale = np.empty((rows, k // FP8_BLOCK), dtype=np.float32)
+    scale = np.empty((rows, k // block), dtype=np.float32)
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
-        w = (w_bits[r0:r1].astype(np.uint32) << 16).view(np.float32).reshape(r1 - r0, k // FP8_BLOCK, FP8_BLOCK)
+        w = (w_bits[r0:r1].astype(np.uint32) << 16).view(np.float32).reshape(r1 - r0, k // block, block)
         amax = np.abs(w).max(axis=2)
         s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
         q[r0:r1] = e4m3_encode((w / s[:, :, None]).astype(np.float32)).reshape(r1 - r0, k)
         scale[r0:r1] = s
     return q, scale
+
+
+def quantize_e4m3_channels(w_bits: np.ndarray, chunk_rows: int = 2048):
+    """Per-output-channel E4M3 storage of a bf16 weight ``[rows, K]``: one scale per row
+    (``amax / 448`` over the row).  Returns ``(codes uint8 [rows, K], scales float32 [rows])``."""
+    q, s = quantize_e4m3_blocks(w_bits, chunk_rows, block=w_bits.shape[1])
+    return q, s[:, 0].copy()
 
 
 # --- The five workloads, as shapes and distributions ---------------------------------
