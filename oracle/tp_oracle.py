@@ -441,8 +441,9 @@ _E4M3_POS_VALS = _E4M3[:0x7F]
 
 
 def e4m3_encode(v32: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 code of float32 values: ties to the code with the even mantissa, and
-    magnitudes of 448 or more saturate to 448 (the format has no infinity).
+    """Nearest E4M3 code of float32 values: ties to the code with the even mantissa,
+    magnitudes of 448 or more saturate to 448 (the format has no infinity), and the sign
+    is the float's sign bit (signed zero).
 
     Follows the OCP 8-bit definition: every finite E4M3 value is a candidate; the nearest one
     wins; on an exact tie the candidate whose 3-bit mantissa is even (code LSB 0) wins, which
@@ -458,7 +459,9 @@ def e4m3_encode(v32: np.ndarray) -> np.ndarray:
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((_E4M3_POS_CODES[hi] & 1) == 0))
     code = np.where(pick_hi, _E4M3_POS_CODES[hi], _E4M3_POS_CODES[lo]).astype(np.uint8)
     code = np.where(mag == _E4M3_POS_VALS[hi], _E4M3_POS_CODES[hi], code).astype(np.uint8)
-    return np.where(v < 0, code | np.uint8(0x80), code).astype(np.uint8)
+    # the code's sign is the float's sign bit: E4M3 has a signed zero, so -0.0 and negative
+    # quotients that round to zero encode as 0x80
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def quantize_rows_e4m3(x_bits):

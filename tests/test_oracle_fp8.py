@@ -17,11 +17,10 @@ def test_encode_matches_torch_float8_cast_in_range():
     g = np.random.default_rng(11)
     v = np.concatenate([g.standard_normal(20000) * 40, g.standard_normal(20000) * 1e-2,
                         g.uniform(-447.9, 447.9, 20000)]).astype(np.float32)
+    v = np.concatenate([v, np.array([0.0, -0.0, -1e-9, 1e-9], np.float32)])
     ours = oracle.e4m3_encode(v)
     ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    # torch writes +0 / -0 by sign; both decode to zero
-    same = (ours == ref) | ((oracle.e4m3_to_f64(ours) == 0) & (oracle.e4m3_to_f64(ref) == 0))
-    assert same.all(), v[~same][:5]
+    assert np.array_equal(ours, ref), v[ours != ref][:5]  # signed zero included
 
 
 def test_encode_is_nearest_by_brute_force():
