@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--parts", default="1,2,3,4,5", help="comma list of workload parts to run")
+    ap.add_argument("--fp8", type=int, default=1, help="1: also time the fp8 prefill column linear (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
@@ -300,6 +301,61 @@ def roofline_leg(wl, launches, stream):
             "algorithmic_bytes_per_launch": (32768 * 8192 + 3072 * 8192 + 32768 * 3072) * 2 if key == 4 else None}
 
 
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA
+
+
+def fp8_prefill_leg(launches, stream):
+    """The fp8 prefill column linear on the RMSNorm workload's shapes (x [32768, 8192], column
+    shard [3072, 8192] quantised per output channel): per-row E4M3 quantisation of x, then the
+    E4M3 x E4M3 GEMM with both scales applied in its epilogue. Each kernel is timed with HIP
+    events on the stream it runs on."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    c = synth.WORKLOADS[4]
+    inp = synth.workload_inputs(4)
+    wq, ws = synth.quantize_e4m3_channels(inp["w"])
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wq_d, ws_d = torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)
+    M, K = x.shape
+    N = wq.shape[0]
+    q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tt.tp_quantize_rows_e4m3(x, q, s)
+        if ev is not None:
+            ev[1].record(stream)
+        tt.tp_column_linear_fp8(q, s, wq_d, ws_d, None, [c["out_logical"]], c["tp"], c["rank"], y=y)
+        if ev is not None:
+            ev[2].record(stream)
+
+    run()
+    run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        run(ev)
+    torch.cuda.synchronize()
+    q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    g_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    flops = 2.0 * M * N * K
+    tf = flops / (g_us * 1e-6) / 1e12
+    q_bytes = M * K * 3 + M * 4  # bf16 read, codes written, scales written
+    return {"workload": "fp8 prefill column shard: quantise x [32768, 8192] per row to E4M3, "
+                        "E4M3 GEMM with W [3072, 8192] (per-channel scales), bf16 out",
+            "quantize_mean_us": round(q_us, 2), "quantize_gbs": round(q_bytes / (q_us * 1e-6) / 1e9, 1),
+            "gemm_mean_us": round(g_us, 2), "gemm_tflops": round(tf, 1),
+            "gemm_frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "peak_fp8_tflops": PEAK_FP8_TFLOPS,
+            "end_to_end_tflops": round(flops / ((q_us + g_us) * 1e-6) / 1e12, 1), "launches_timed": launches}
+
+
 def copy_probe(mb: int):
     """Plain device-to-device copies of a known size: the reference for HBM byte counters."""
     import torch
@@ -399,6 +455,7 @@ def main():
 
     value = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
     roofline = roofline_leg(wl, args.steps, stream) if gemm_ms > 0 else None
+    fp8 = fp8_prefill_leg(args.steps, stream) if args.fp8 else None
     out = {
         "metric": METRIC, "value": round(value, 2) if value else None, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -411,6 +468,7 @@ def main():
                    "parts": sorted(parts)},
         "roofline": roofline,
         "lm_head": lm or None,
+        "fp8_prefill": fp8,
         "per_config": per_config,
     }
     if args.cpu_seconds > 0:

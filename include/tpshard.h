@@ -116,6 +116,43 @@ TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_s
                      int y_dtype, int layout, int64_t ldy, void* stream);
 
 /*
+ * tp_quantize_rows_e4m3 - per-row (per-token) E4M3 quantisation of bf16 activations, the
+ * first step of the fp8 prefill linear below.
+ *
+ * [palm] transformer_layer_weight_gathered: a QuantizedLayer multiplies by quantised
+ * weights and applies the per-output-channel scale to the matmul result. To run that
+ * product on fp8 matrix cores the activations are quantised too, one scale per row:
+ * scale[m] = amax_k |x[m,k]| / 448 (1 for an all-zero row), q[m,k] = e4m3(x[m,k] / scale[m]),
+ * both divisions IEEE float32 (nearest even), the code the nearest E4M3 value (ties to the
+ * even mantissa, 448 and beyond saturate to 448, sign from the float's sign bit).
+ *
+ * x      device bf16 [M, K], 16-byte aligned; K % 8 == 0
+ * q      device uint8 [M, K] (OCP E4M3FN codes), 16-byte aligned
+ * scale  device f32 [M]
+ * M = 0 enqueues nothing. Errors: TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED (K % 8,
+ * misalignment), TP_ERR_HIP.
+ */
+TP_API int tp_quantize_rows_e4m3(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream);
+
+/*
+ * tp_column_linear_fp8 - tp_column_linear on E4M3 activations and weights (fp8 prefill).
+ *
+ * [palm] QuantizedLayer: y = round(act(x_scale[m] * w_scale[j] * sum_k q_x[m,k] q_w[j,k]
+ * + b[j])), the product of E4M3 values accumulated in float32 on the fp8 matrix cores, the
+ * per-output-channel weight scale (and the per-row activation scale) applied to the product.
+ *
+ * x_q       device uint8 [M, K]: E4M3 codes (tp_quantize_rows_e4m3), x_scale device f32 [M]
+ * w_q       device uint8 [N_r, K]: E4M3 codes of the rank's weight rows, w_scale f32 [N_r]
+ *           (one scale per output channel), same row map as tp_column_linear
+ * K % 64 == 0. Everything else (bias, act, y, y_dtype, layout, ldy, M = 0) as
+ * tp_column_linear. Errors: as tp_column_linear, TP_ERR_UNSUPPORTED for K % 64.
+ */
+TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
+                                const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes,
+                                int n_sub, int tp_size, int rank, int act, void* y, int y_dtype, int layout,
+                                int64_t ldy, void* stream);
+
+/*
  * tp_row_linear_partial - one rank's row-parallel partial sum, before any reduction.
  *
  * [nanotron] TensorParallelRowLinear (the MLP's c_proj, the attention's output

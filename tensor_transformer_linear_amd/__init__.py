@@ -31,6 +31,9 @@ SIGNATURES = {
     "tp_shard_widths": (_int, [_P64, _int, _int, _int, _P64, _P64, _P64, _P64]),
     "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int, _int, _i64, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _int, _vp, _int, _vp]),
+    "tp_quantize_rows_e4m3": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "tp_column_linear_fp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int,
+                                    _int, _i64, _vp]),
     "tp_rmsnorm_workspace_bytes": (_sz, [_i64, _i64]),
     "tp_rmsnorm_workspace_min_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_column_linear": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _P64, _int, _int, _int,
@@ -120,6 +123,33 @@ def tp_column_linear(x, w_shard, bias_shard, subparam_sizes, tp_size, rank, act=
         ldy = y.stride(0) if y.dim() == 2 else y.shape[-1]
     _check(lib().tp_column_linear(_ptr(x), M, K, _ptr(w_shard), _ptr(bias_shard), sizes, n, tp_size, rank, act,
                                   _ptr(y), y_dtype, layout, ldy, _stream(stream)))
+    return y
+
+
+def tp_quantize_rows_e4m3(x, q=None, scale=None, stream=None):
+    """Per-row E4M3 codes of bf16 ``x`` and their float32 scales; returns ``(q uint8, scale f32)``."""
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib().tp_quantize_rows_e4m3(_ptr(x), M, K, _ptr(q), _ptr(scale), _stream(stream)))
+    return q, scale
+
+
+def tp_column_linear_fp8(x_q, x_scale, w_q, w_scale, bias_shard, subparam_sizes, tp_size, rank, act=TP_ACT_NONE,
+                         y=None, y_dtype=TP_DTYPE_BF16, layout=TP_LAYOUT_LOCAL, ldy=None, stream=None):
+    """``tp_column_linear`` on E4M3 codes: ``act(x_scale * w_scale * (x_q @ w_q.T) + bias)``; returns ``y``."""
+    M, K = x_q.shape
+    sizes, n = _i64_array(subparam_sizes)
+    if y is None:
+        width = int(w_q.shape[0]) if layout == TP_LAYOUT_LOCAL else sum(int(s) for s in subparam_sizes)
+        dt = torch.bfloat16 if y_dtype == TP_DTYPE_BF16 else torch.float32
+        y = (torch.empty if layout == TP_LAYOUT_LOCAL else torch.zeros)((M, width), dtype=dt, device=x_q.device)
+    if ldy is None:
+        ldy = y.stride(0) if y.dim() == 2 else y.shape[-1]
+    _check(lib().tp_column_linear_fp8(_ptr(x_q), _ptr(x_scale), M, K, _ptr(w_q), _ptr(w_scale), _ptr(bias_shard),
+                                      sizes, n, tp_size, rank, act, _ptr(y), y_dtype, layout, ldy, _stream(stream)))
     return y
 
 

@@ -96,6 +96,12 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
             break;
           }
         const bool whole = col + 4 <= seg_end && col + 4 <= N;
+        if (ep.row_scale != nullptr) {  // fp8: dequantise the product
+          const float rs = ep.row_scale[row];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < N) val[e] *= rs * ep.col_scale[col + e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (ep.bias != nullptr && col + e < N) val[e] += bf16_to_f32(ep.bias[col + e]);
@@ -303,18 +309,26 @@ __device__ __forceinline__ int dma_off(int row, int c) { return row * DROW + ((c
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma_load16(const uint16_t* g, lds_byte* lds) {
+__device__ __forceinline__ void dma_load16(const void* g, lds_byte* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
 // SCHED selects the main-loop schedule: 0 = every wave multiplies while its own next reads fly
 // (fragments double-buffered in registers); 1 = ping-pong between two groups of four waves (one
 // wave per SIMD each, eight waves per workgroup): one group multiplies while the other reads
 // its next fragments from LDS and issues the next global loads, and the roles swap at every
 // barrier, so each SIMD always has a wave issuing MFMAs.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED>
+//
+// FP8: A and B are E4M3 codes. A stage still holds 64 bytes of every row (64 K values instead
+// of 32) and one v_mfma_f32_32x32x64_f8f6f4 per 32x32 block takes the place of the two bf16
+// MFMAs: lane l supplies 32 consecutive K bytes (chunks 2 (l / 32) and 2 (l / 32) + 1 of the
+// row), the same for A and B. Only the ping-pong schedule handles it.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED, bool FP8 = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                             int group_m) {
+  static_assert(!FP8 || SCHED == 1, "the fp8 path runs the ping-pong schedule");
   constexpr int NT = WAVES_M * WAVES_N * 64;
   constexpr int NWAVE = NT / 64;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -339,10 +353,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   const int in = lid - grp * per_group;
   const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * BN;
   const int M = p.M, N = p.N, K = p.K;
-  const int nk = K / DBK;
+  constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
+  const int nk = K / (DROW / ESZ);    // a stage is 64 bytes of every row
 
   // Per DMA block this wave issues: the global source of this lane's 16 bytes.
-  const uint16_t* src[BLK_PER_WAVE];
+  const unsigned char* src[BLK_PER_WAVE];
   int dst[BLK_PER_WAVE];
 #pragma unroll
   for (int b = 0; b < BLK_PER_WAVE; ++b) {
@@ -351,10 +366,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     const int c = (lane & 3) ^ ((row >> 2) & 3);  // logical chunk stored at this lane's slot
     if (blk < NBLK_A) {
       const int gm = min(m0 + row, M - 1);
-      src[b] = p.A + (int64_t)gm * p.lda + c * 8;
+      src[b] = reinterpret_cast<const unsigned char*>(p.A) + ((int64_t)gm * p.lda) * ESZ + c * 16;
     } else {
       const int gn = blk < NBLK ? min(n0 + row, N - 1) : 0;
-      src[b] = p.B + (int64_t)gn * p.ldb + c * 8;
+      src[b] = reinterpret_cast<const unsigned char*>(p.B) + ((int64_t)gn * p.ldb) * ESZ + c * 16;
     }
     dst[b] = blk * 1024;
   }
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
     lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
 #pragma unroll
-    for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + kt * DBK, base + dst[b]);
+    for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + (int64_t)kt * DROW, base + dst[b]);
   };
 
   f32x16_t acc[FM][FN];
@@ -376,16 +391,32 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   struct Frag {
     bf16x8_t a[FM], b[FN];
   };
+  // bf16: fragment `half` is the 16-wide half of the stage (chunk 2 half + l / 32); fp8: it is
+  // one of the two 16-byte chunks of the lane's 32 K bytes (chunk 2 (l / 32) + half).
   auto read = [&](Frag& f, int stage, int half) {
     const unsigned char* sa = smem + stage * STAGE;
     const unsigned char* sb = sa + BM * DROW;
+    const int chunk = FP8 ? khalf * 2 + half : half * 2 + khalf;
     static_for<FM>([&](auto i) {
-      f.a[i] = __builtin_bit_cast(bf16x8_t,
-                                  *reinterpret_cast<const u32x4_t*>(sa + dma_off(a_row0 + i * 32, half * 2 + khalf)));
+      f.a[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sa + dma_off(a_row0 + i * 32, chunk)));
     });
     static_for<FN>([&](auto j) {
-      f.b[j] = __builtin_bit_cast(bf16x8_t,
-                                  *reinterpret_cast<const u32x4_t*>(sb + dma_off(b_row0 + j * 32, half * 2 + khalf)));
+      f.b[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(sb + dma_off(b_row0 + j * 32, chunk)));
+    });
+  };
+  // fp8: one MFMA per 32x32 block over the stage's 64 K values, operands from both fragments
+  auto mma8 = [&](const Frag& f0, const Frag& f1) {
+    static_for<FM>([&](auto i) {
+      static_for<FN>([&](auto j) {
+        const i32x8_t a = __builtin_bit_cast(
+            i32x8_t, __builtin_shufflevector(__builtin_bit_cast(u32x4_t, f0.a[i]), __builtin_bit_cast(u32x4_t, f1.a[i]),
+                                             0, 1, 2, 3, 4, 5, 6, 7));
+        const i32x8_t b = __builtin_bit_cast(
+            i32x8_t, __builtin_shufflevector(__builtin_bit_cast(u32x4_t, f0.b[j]), __builtin_bit_cast(u32x4_t, f1.b[j]),
+                                             0, 1, 2, 3, 4, 5, 6, 7));
+        // E4M3 x E4M3 (format selectors 0), unit block scales
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+      });
     });
   };
   auto mma = [&](const Frag& f) {
@@ -437,8 +468,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       issue(kt + STAGES - 1);
       wait_barrier(std::integral_constant<int, (STAGES - 2) * BLK_PER_WAVE>{}, std::integral_constant<int, 0>{});
       __builtin_amdgcn_s_setprio(1);  // the multiplying wave first: the other group only issues memory work
-      mma(f0);
-      mma(f1);
+      if constexpr (FP8) {
+        mma8(f0, f1);
+      } else {
+        mma(f0);
+        mma(f1);
+      }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
@@ -453,6 +488,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     return;
   }
 
+  if constexpr (!FP8) {
   // Software pipeline over K steps, two register sets of fragments. Step kt enters with the
   // first half of stage kt in f0; it reads the second half into f1 and multiplies f0 (the
   // MFMAs cover the LDS latency); waits until stage kt + 1 has landed in every wave (at most
@@ -486,6 +522,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   }
   __syncthreads();
   gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED = 0>
@@ -508,7 +545,32 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BM, int BN>
+hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int group_m = tiles_m < 4 ? tiles_m : 4;
+  hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
+                     tiles_m, tiles_n, group_m);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_fp8_pick_tile(int M, int N, int K) {
+  (void)K;
+  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+  return t256 >= 192 ? TILE_256x256 : TILE_128x128;
+}
+
+hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
+  if (!p.fp8 || p.K % 64 != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0 || p.row_r != nullptr) return hipErrorInvalidValue;
+  if (tile == TILE_AUTO) tile = gemm_fp8_pick_tile(p.M, p.N, p.K);
+  switch (tile) {
+    case TILE_256x256: return launch_tile_fp8<256, 256>(p, stream);
+    case TILE_128x128: return launch_tile_fp8<128, 128>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;

@@ -19,14 +19,17 @@ struct GemmEpilogue {
   int n_seg;             // column segments; 0 = output column is the local column
   int seg_end[TP_MAX_SUBPARAMS];    // exclusive local end column of each segment
   int seg_delta[TP_MAX_SUBPARAMS];  // output column minus local column inside the segment
+  const float* row_scale;  // f32 [M] or nullptr: acc * row_scale[m] * col_scale[n] before the bias
+  const float* col_scale;  // f32 [N] (with row_scale)
 };
 
 // C[M,N] = A[M,K] * B[N,K]^T with both operands K-contiguous (weights as stored).
 struct GemmProblem {
-  const uint16_t* A;  // bf16 [M, lda]
-  int64_t lda;
-  const uint16_t* B;  // bf16 [N, ldb]
+  const uint16_t* A;  // bf16 [M, lda] (E4M3 bytes when fp8)
+  int64_t lda;        // elements
+  const uint16_t* B;  // bf16 [N, ldb] (E4M3 bytes when fp8)
   int64_t ldb;
+  int fp8;            // 1: A and B are OCP E4M3 codes (direct-to-LDS path only, K % 64 == 0)
   int M, N, K;
   // Optional RMSNorm applied to A while it is staged: a' = bf16(bf16(a * row_r[m]) * col_t[k]),
   // or bf16(a * row_r[m]) when col_t is null.
@@ -54,6 +57,13 @@ enum GemmPath : int { GEMM_PATH_AUTO = -1, GEMM_PATH_REGISTER = 0, GEMM_PATH_DMA
 
 hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream);
 int gemm_pick_tile(int M, int N, int K);
+// E4M3 x E4M3 GEMM (p.fp8 = 1) on the fp8 matrix cores; tile: TILE_AUTO, TILE_256x256 or TILE_128x128.
+hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream);
+int gemm_fp8_pick_tile(int M, int N, int K);
+
+// Per-row E4M3 quantisation of bf16 activations: scale[m] = amax/448 (1 for a zero row),
+// q = nearest E4M3 code of x / scale (ties to even, saturating, signed zero). K % 8 == 0.
+hipError_t launch_quantize_rows_e4m3(const uint16_t* x, int M, int K, uint8_t* q, float* scale, hipStream_t stream);
 
 // RMSNorm statistics: r[m] = rsqrt(mean_k x^2 + eps) for every row, t[k] = bf16(1 + s[k]),
 // and, when xnorm is non-null, the normalised bf16 rows.

@@ -162,6 +162,41 @@ TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_s
   return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_column_linear launch");
 }
 
+TP_API int tp_quantize_rows_e4m3(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream) {
+  if (M < 0 || K <= 0) return fail(TP_ERR_INVALID_ARG, "M = %lld, K = %lld: need M >= 0, K > 0", (long long)M, (long long)K);
+  if (M > 0 && (x == nullptr || q == nullptr || scale == nullptr))
+    return fail(TP_ERR_INVALID_ARG, "x, q and scale must be non-NULL");
+  if (M > INT_MAX || K > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and K must fit in 31 bits");
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4))
+    return fail(TP_ERR_UNSUPPORTED, "x and q must be 16-byte aligned, scale 4-byte aligned");
+  if (M == 0) return ok();
+  return hip_status(tpk::launch_quantize_rows_e4m3(static_cast<const uint16_t*>(x), (int)M, (int)K,
+                                                   static_cast<uint8_t*>(q), scale, as_stream(stream)),
+                    "tp_quantize_rows_e4m3 launch");
+}
+
+TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
+                                const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                                int tp_size, int rank, int act, void* y, int y_dtype, int layout, int64_t ldy,
+                                void* stream) {
+  tpk::GemmProblem p;
+  int st = prepare_column(x_q, M, K, w_q, bias_shard, subparam_sizes, n_sub, tp_size, rank, act, y, y_dtype, layout,
+                          ldy, &p);
+  if (st != TP_OK) return st;
+  if (K % 64) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 64 for the fp8 path", (long long)K);
+  if (w_scale == nullptr || (M > 0 && x_scale == nullptr))
+    return fail(TP_ERR_INVALID_ARG, "x_scale and w_scale must be non-NULL");
+  if (!aligned(x_scale, 4) || !aligned(w_scale, 4)) return fail(TP_ERR_UNSUPPORTED, "scales must be 4-byte aligned");
+  if (M == 0) return ok();
+  p.fp8 = 1;
+  p.ep.row_scale = x_scale;
+  p.ep.col_scale = w_scale;
+  const int tile = g_tile_override == tpk::TILE_256x256 || g_tile_override == tpk::TILE_128x128 ? g_tile_override
+                                                                                                   : tpk::TILE_AUTO;
+  return hip_status(tpk::launch_gemm_fp8(p, tile, as_stream(stream)), "tp_column_linear_fp8 launch");
+}
+
 TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
                           const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream) {
   if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);

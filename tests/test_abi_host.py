@@ -195,3 +195,47 @@ def test_product_path_does_not_use_the_oracle_or_generator():
                 text = open(os.path.join(root, f)).read()
                 for word in ("import oracle", "from oracle", "import synth", "from synth", "tp_oracle"):
                     assert word not in text, (f, word)
+
+
+def quant(**kw):
+    a = dict(x=A, M=16, K=128, q=A2, s=A3)
+    a.update(kw)
+    return L.tp_quantize_rows_e4m3(a["x"], a["M"], a["K"], a["q"], a["s"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(q=None), tt.TP_ERR_INVALID_ARG), (dict(s=None), tt.TP_ERR_INVALID_ARG),
+    (dict(M=-1), tt.TP_ERR_INVALID_ARG), (dict(K=0), tt.TP_ERR_INVALID_ARG), (dict(K=12), tt.TP_ERR_UNSUPPORTED),
+    (dict(x=MIS), tt.TP_ERR_UNSUPPORTED), (dict(q=MIS), tt.TP_ERR_UNSUPPORTED), (dict(M=2 ** 31), tt.TP_ERR_UNSUPPORTED),
+])
+def test_quantize_rows_rejects(kw, status):
+    assert quant(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_quantize_rows_empty_input_is_a_no_op():
+    assert quant(M=0, x=None, q=None, s=None) == tt.TP_OK
+
+
+def col8(**kw):
+    a = dict(x=A, xs=A, M=64, K=128, w=A2, ws=A2, b=None, sizes=[64, 32, 32], tp=2, rank=0, act=0, y=A3, yd=0,
+             layout=0, ldy=64)
+    a.update(kw)
+    s = a["sizes"]
+    return L.tp_column_linear_fp8(a["x"], a["xs"], a["M"], a["K"], a["w"], a["ws"], a["b"], _sizes(s), len(s), a["tp"],
+                                  a["rank"], a["act"], a["y"], a["yd"], a["layout"], a["ldy"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(xs=None), tt.TP_ERR_INVALID_ARG), (dict(ws=None), tt.TP_ERR_INVALID_ARG),
+    (dict(w=None), tt.TP_ERR_INVALID_ARG), (dict(K=96), tt.TP_ERR_UNSUPPORTED), (dict(K=12), tt.TP_ERR_UNSUPPORTED),
+    (dict(sizes=[64, 1, 32]), tt.TP_ERR_SHAPE), (dict(ldy=56), tt.TP_ERR_SHAPE), (dict(rank=2), tt.TP_ERR_INVALID_ARG),
+    (dict(xs=ctypes.c_void_p(0x10001)), tt.TP_ERR_UNSUPPORTED), (dict(yd=2), tt.TP_ERR_UNSUPPORTED),
+])
+def test_column_linear_fp8_rejects(kw, status):
+    assert col8(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_column_linear_fp8_empty_input_is_a_no_op():
+    assert col8(M=0, x=None, xs=None, y=None) == tt.TP_OK

@@ -1,0 +1,154 @@
+"""fp8 prefill column linear on the GPU against the oracle: per-row E4M3 activation codes and
+scales bit for bit, the E4M3 x E4M3 product exact on integer codes with power-of-two scales,
+within tolerance on gaussian inputs with bias, GELU and LOGICAL placement, on both fp8 tiles,
+and on sampled rows of the RMSNorm workload's shape."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tensor_transformer_linear_amd as tt
+from helpers import assert_close, dev_bf16, dev_f32, dev_u8, host_bits, host_f32
+
+pytestmark = pytest.mark.gpu
+
+TILES = [0, 2]  # 256x256 (ping-pong, 8 waves) and 128x128
+
+# The fp8 matrix instruction (v_mfma_f32_32x32x64_f8f6f4) sums its 64 products with about 16
+# significant bits (measured: 1.5e-5 rms and 1e-4 max of rms(ref) on gaussian operands, where
+# the bf16 instruction on the same values is at 4e-8). Well inside the 2e-2 * rms bound, but it
+# moves about 1 % of bf16 outputs across a rounding boundary: up to 5 % may sit one ulp off.
+FP8_STRADDLE = 0.05
+FP8_F32_TOL = 1e-3  # float32 outputs: max |err| <= 1e-3 * rms, a tighter guard on the product
+
+
+def _special_rows(K, seed):
+    g = np.random.default_rng(seed)
+    x = synth.bf16_normal((12, K), 1.0, 950 + seed, 0)
+    x[0] = 0                                                     # all-zero row: scale 1, codes 0
+    x[1] = 0x8000                                                # all -0.0: codes 0x80
+    x[2] = 0; x[2, K // 2] = synth.bf16_from_float(np.array([-7.5]))[0]   # one-hot
+    x[3] = synth.bf16_from_float(np.full(K, 3.0))              # constant: every code 0x7E
+    x[4] = synth.bf16_from_float((g.standard_normal(K) * 1e4).astype(np.float32))
+    x[5] = synth.bf16_from_float((g.standard_normal(K) * 1e-6).astype(np.float32))
+    big = np.ones(K, np.float32); big[0] = 1e6                 # most quotients deep in the subnormals
+    x[6] = synth.bf16_from_float(big)
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(12, 8), (12, 200), (12, 8192), (12, 9000)])
+def test_quantize_rows_bitexact_special_rows(M, K):
+    x = _special_rows(K, K)
+    q, s = tt.tp_quantize_rows_e4m3(dev_bf16(x))
+    rq, rs = oracle.quantize_rows_e4m3(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantize_rows_bitexact_gaussian_and_ragged():
+    x = synth.bf16_normal((777, 1032), 1.0, 951, 0)
+    q, s = tt.tp_quantize_rows_e4m3(dev_bf16(x))
+    rq, rs = oracle.quantize_rows_e4m3(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy(), rs)
+
+
+def test_quantize_rows_every_bf16_value():
+    # every finite bf16 pattern, in rows of 256 that share one scale: all code paths of the encoder
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((pats >> 7) & 0xFF) != 0xFF
+    v = pats[finite]
+    v = v[: (v.size // 256) * 256].reshape(-1, 256)
+    q, s = tt.tp_quantize_rows_e4m3(dev_bf16(v))
+    rq, rs = oracle.quantize_rows_e4m3(v)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,sizes,tp,rank,K", [(300, [120, 80], 1, 0, 320), (64, [512, 256, 256], 2, 1, 128),
+                                                (1000, [2048], 8, 3, 64)])
+def test_fp8_linear_exact_on_integer_codes(tile, M, sizes, tp, rank, K):
+    g = np.random.default_rng(M + K)
+    ints = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
+    total = tt.tp_shard_widths(sizes, tp, rank)[3]
+    xq = oracle.e4m3_encode(g.choice(ints, (M, K)))
+    wq = oracle.e4m3_encode(g.choice(ints, (total, K)))
+    xs = (2.0 ** g.integers(-4, 4, M)).astype(np.float32)
+    ws = (2.0 ** g.integers(-4, 4, total)).astype(np.float32)
+    tt.set_gemm_tile(tile)
+    try:
+        y = tt.tp_column_linear_fp8(dev_u8(xq), dev_f32(xs), dev_u8(wq), dev_f32(ws), None, sizes, tp, rank,
+                                    y_dtype=tt.TP_DTYPE_F32)
+    finally:
+        tt.set_gemm_tile(-1)
+    ref = oracle.column_linear_fp8(xq, xs, wq, ws, None, sizes, tp, rank, out_dtype=oracle.OUT_F32)
+    assert np.array_equal(host_f32(y), ref)
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_fp8_linear_gaussian_bias_gelu_logical(tile):
+    M, K, sizes, tp, rank = 517, 640, [4096, 1024, 1024], 8, 2
+    x = synth.bf16_normal((M, K), 1.0, 952, 0)
+    rows = oracle.shard_rows(sizes, tp, rank)
+    w = synth.bf16_normal((len(rows), K), 0.02, 952, 1)
+    b = synth.bf16_normal((len(rows),), 0.02, 952, 2)
+    wq, ws = synth.quantize_e4m3_channels(w)
+    tt.set_gemm_tile(tile)
+    try:
+        xq, xs = tt.tp_quantize_rows_e4m3(dev_bf16(x))
+        y = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), dev_bf16(b), sizes, tp, rank,
+                                    act=tt.TP_ACT_GELU_ERF)
+        ylog = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), dev_bf16(b), sizes, tp, rank,
+                                       act=tt.TP_ACT_GELU_ERF, layout=tt.TP_LAYOUT_LOGICAL)
+    finally:
+        tt.set_gemm_tile(-1)
+    rq, rs = oracle.quantize_rows_e4m3(x)
+    assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
+    ref = oracle.column_linear_fp8(rq, rs, wq, ws, b, sizes, tp, rank, act=oracle.ACT_GELU)
+    assert_close(host_bits(y), ref, what="fp8 local", straddle=FP8_STRADDLE)
+    assert np.array_equal(host_bits(ylog)[:, rows], host_bits(y))   # LOGICAL = LOCAL scattered, bit for bit
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_fp8_linear_f32_output_accuracy(tile):
+    M, K, N = 300, 1024, 640
+    x = synth.bf16_normal((M, K), 1.0, 953, 0)
+    w = synth.bf16_normal((N, K), 0.02, 953, 1)
+    wq, ws = synth.quantize_e4m3_channels(w)
+    rq, rs = oracle.quantize_rows_e4m3(x)
+    tt.set_gemm_tile(tile)
+    try:
+        y = tt.tp_column_linear_fp8(dev_u8(rq), dev_f32(rs), dev_u8(wq), dev_f32(ws), None, [N], 1, 0,
+                                    y_dtype=tt.TP_DTYPE_F32)
+    finally:
+        tt.set_gemm_tile(-1)
+    ref = oracle.column_linear_fp8(rq, rs, wq, ws, None, [N], 1, 0, out_dtype=oracle.OUT_F32)
+    assert_close(host_f32(y), ref, tol=FP8_F32_TOL, what="fp8 f32 out")
+
+
+def test_fp8_linear_empty_input():
+    w = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
+    ws = torch.ones(64, dtype=torch.float32, device="cuda")
+    y = tt.tp_column_linear_fp8(torch.empty((0, 128), dtype=torch.uint8, device="cuda"),
+                                torch.empty(0, dtype=torch.float32, device="cuda"), w, ws, None, [64], 1, 0)
+    assert y.shape == (0, 64)
+
+
+def test_fp8_prefill_workload4_shape_sampled_rows():
+    """The RMSNorm workload's column shard [3072, 8192] on its 32768 x rows, fp8: codes of the
+    sampled rows bit for bit, outputs within tolerance."""
+    c = synth.WORKLOADS[4]
+    inp = synth.workload_inputs(4)
+    x, w = inp["x"], inp["w"]
+    wq, ws = synth.quantize_e4m3_channels(w)
+    xq, xs = tt.tp_quantize_rows_e4m3(dev_bf16(x))
+    y = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), None, [c["out_logical"]], c["tp"], c["rank"])
+    g = np.random.default_rng(9)
+    sr = np.unique(np.concatenate([np.arange(8), np.arange(x.shape[0] - 8, x.shape[0]), g.integers(0, x.shape[0], 24)]))
+    rq, rs = oracle.quantize_rows_e4m3(x[sr])
+    idx = torch.from_numpy(sr).cuda()
+    assert np.array_equal(xq[idx].cpu().numpy(), rq) and np.array_equal(xs[idx].cpu().numpy(), rs)
+    ref = oracle.column_linear_fp8(rq, rs, wq, ws, None, [c["out_logical"]], c["tp"], c["rank"])
+    assert_close(host_bits(y[idx]), ref, what="fp8 workload-4 rows", straddle=FP8_STRADDLE)

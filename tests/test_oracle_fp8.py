@@ -131,3 +131,19 @@ def test_channel_quantised_weights_decode_within_half_a_step():
     assert np.all(np.abs(rec - wf) <= bound)
     # the generator's encoder and the oracle's agree on the stored codes
     assert np.array_equal(q, oracle.e4m3_encode((wf / s[:, None]).astype(np.float32)))
+
+
+def test_tolerance_helper_accepts_rare_one_ulp_straddles_only():
+    import helpers
+    ref = synth.bf16_normal((100, 100), 1.0, 904, 0)
+    got = ref.copy()
+    got.flat[[3, 77]] += 1                       # two rounding straddles: accepted
+    helpers.assert_close(got, ref)
+    bad = ref.copy()
+    bad.flat[5] ^= 0x4000                         # a large error elsewhere: rejected
+    with pytest.raises(AssertionError):
+        helpers.assert_close(bad, ref)
+    many = ref.copy()
+    many.flat[:50] += 1                           # 0.5 % of outputs one ulp off: rejected
+    with pytest.raises(AssertionError):
+        helpers.assert_close(many, ref)
