@@ -517,3 +517,28 @@ def column_linear_fp8(xq, x_scale, wq_shard, w_scale_shard, bias_shard_bits, sub
         out[:, lo:lo + wd] = y[:, lc:lc + wd]
         mask[lo:lo + wd] = True
     return out, mask
+
+
+# --------------------------------------------------------------------------------------
+# F4 - vocab-parallel embedding lookup  [palm] embed_manual
+# --------------------------------------------------------------------------------------
+
+def embed_shard(tokens, vocab: int, tp_size: int, rank: int, table_bits):
+    """One rank's share of the embedding lookup.
+
+    [palm] ``embed_manual``: each device holds the rows of its vocab shard; a token's id minus
+    the shard's first id indexes the table, and tokens outside the shard give a zero row, so
+    summing the ranks' outputs (the page's reduce-scatter) yields the full lookup.  Shards
+    follow ``vocab_shard`` (the LM head's split).  Reading: ids outside ``[0, vocab)`` give a
+    zero row on every rank.  Returns bf16 bits ``[n_tokens, E]``.
+    """
+    tok = np.asarray(tokens, dtype=np.int64).reshape(-1)
+    rows, off = vocab_shard(vocab, tp_size, rank)
+    tbl = np.asarray(table_bits, dtype=np.uint16)
+    if tbl.shape[0] != rows:
+        raise ValueError(f"table has {tbl.shape[0]} rows, the shard has {rows}")
+    local = tok - off
+    hit = (local >= 0) & (local < rows) & (tok >= 0) & (tok < vocab)
+    out = np.zeros((tok.size, tbl.shape[1]), dtype=np.uint16)
+    out[hit] = tbl[local[hit]]
+    return out
