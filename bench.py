@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--parts", default="1,2,3,4,5", help="comma list of workload parts to run")
-    ap.add_argument("--fp8", type=int, default=1, help="1: also time the fp8 prefill column linear (0 = skip)")
+    ap.add_argument("--fp8", type=int, default=1,
+                    help="1: also time the next-row legs, the fp8 prefill column linear and the embedding (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
@@ -356,6 +357,39 @@ def fp8_prefill_leg(launches, stream):
             "end_to_end_tflops": round(flops / ((q_us + g_us) * 1e-6) / 1e12, 1), "launches_timed": launches}
 
 
+def embedding_leg(launches, stream):
+    """The vocab-parallel embedding (one rank's share) at the RMSNorm workload's prefill size:
+    32768 token ids uniform over a 128256-token vocabulary, tp 8 rank 0 (16032 table rows of
+    8192 bf16), so one token in eight reads a table row and every token writes an output row."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    vocab, tp, rank, E, n = 128256, 8, 0, 8192, 16 * 2048
+    rows = vocab // tp
+    dev = torch.device("cuda:0")
+    tbl = torch.from_numpy(synth.bf16_normal((rows, E), 1.0, 6, 1).view(np.int16)).view(torch.bfloat16).to(dev)
+    tok = torch.from_numpy(synth.rng(6, 0).integers(0, vocab, n).astype(np.int32)).to(dev)
+    out = torch.empty((n, E), dtype=torch.bfloat16, device=dev)
+    hits = int(((tok >= 0) & (tok < rows)).sum().item())
+    for _ in range(2):
+        tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = hits * E * 2 + n * 4 + n * E * 2
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "vocab-parallel embedding, 32768 tokens, E 8192, vocab 128256, tp 8 rank 0",
+            "mean_us": round(us, 2), "bytes": nbytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "rows_read": hits, "launches_timed": launches}
+
+
 def copy_probe(mb: int):
     """Plain device-to-device copies of a known size: the reference for HBM byte counters."""
     import torch
@@ -456,6 +490,7 @@ def main():
     value = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
     roofline = roofline_leg(wl, args.steps, stream) if gemm_ms > 0 else None
     fp8 = fp8_prefill_leg(args.steps, stream) if args.fp8 else None
+    emb = embedding_leg(args.steps, stream) if args.fp8 else None
     out = {
         "metric": METRIC, "value": round(value, 2) if value else None, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -469,6 +504,7 @@ def main():
         "roofline": roofline,
         "lm_head": lm or None,
         "fp8_prefill": fp8,
+        "embedding": emb,
         "per_config": per_config,
     }
     if args.cpu_seconds > 0:

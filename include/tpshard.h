@@ -153,6 +153,23 @@ TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M
                                 int64_t ldy, void* stream);
 
 /*
+ * tp_vocab_embedding - one rank's share of the vocab-parallel embedding lookup.
+ *
+ * [palm] embed_manual: each device holds the embedding rows of its vocab shard; a token id
+ * minus the shard's first id indexes the table, and tokens outside the shard give a zero
+ * row, so the ranks' outputs sum (the page's reduce-scatter) to the full lookup.
+ *
+ * tokens       device int32 [n_tokens]; ids outside [0, vocab) give a zero row on every rank
+ * vocab, tp_size, rank  the shard is tp_shard_widths({vocab}, ...): rows [off, off + V_r)
+ * table_shard  device bf16 [V_r, E], 16-byte aligned; E % 8 == 0
+ * out          device bf16 [n_tokens, E], 16-byte aligned
+ * n_tokens = 0 enqueues nothing. Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE (vocab < tp_size),
+ * TP_ERR_UNSUPPORTED (E % 8, misalignment, sizes beyond 31 bits), TP_ERR_HIP.
+ */
+TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,
+                              const void* table_shard, int64_t E, void* out, void* stream);
+
+/*
  * tp_row_linear_partial - one rank's row-parallel partial sum, before any reduction.
  *
  * [nanotron] TensorParallelRowLinear (the MLP's c_proj, the attention's output

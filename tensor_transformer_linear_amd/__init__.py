@@ -32,6 +32,7 @@ SIGNATURES = {
     "tp_column_linear": (_int, [_vp, _i64, _i64, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int, _int, _i64, _vp]),
     "tp_row_linear_partial": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _int, _int, _vp, _int, _vp]),
     "tp_quantize_rows_e4m3": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "tp_vocab_embedding": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp]),
     "tp_column_linear_fp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int,
                                     _int, _i64, _vp]),
     "tp_rmsnorm_workspace_bytes": (_sz, [_i64, _i64]),
@@ -124,6 +125,17 @@ def tp_column_linear(x, w_shard, bias_shard, subparam_sizes, tp_size, rank, act=
     _check(lib().tp_column_linear(_ptr(x), M, K, _ptr(w_shard), _ptr(bias_shard), sizes, n, tp_size, rank, act,
                                   _ptr(y), y_dtype, layout, ldy, _stream(stream)))
     return y
+
+
+def tp_vocab_embedding(tokens, vocab, tp_size, rank, table_shard, out=None, stream=None):
+    """The rank's embedding rows of int32 ``tokens`` (zero rows outside its vocab shard); returns ``out``."""
+    n = tokens.numel()
+    E = table_shard.shape[1]
+    if out is None:
+        out = torch.empty((n, E), dtype=torch.bfloat16, device=table_shard.device)
+    _check(lib().tp_vocab_embedding(_ptr(tokens), n, vocab, tp_size, rank, _ptr(table_shard), E, _ptr(out),
+                                    _stream(stream)))
+    return out
 
 
 def tp_quantize_rows_e4m3(x, q=None, scale=None, stream=None):

@@ -1,0 +1,51 @@
+// Vocab-parallel embedding lookup: one rank's share.
+//
+// [palm] embed_manual: the device holds the rows of its vocab shard; a token's id minus the
+// shard's first id indexes the table, and tokens outside the shard give a zero row, so the
+// ranks' outputs sum (the page's reduce-scatter) to the full lookup. Ids outside [0, vocab)
+// give a zero row on every rank.
+//
+// HBM-bound: a token reads one table row (only when it falls in the shard) and writes one
+// output row. One wave per token; each lane moves 16 bytes per step, so a row of E bf16
+// values takes E / 512 steps, four rows in flight per workgroup.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+namespace {
+
+constexpr int EMB_WAVES = 4;
+
+__global__ __launch_bounds__(EMB_WAVES * 64) void embed_shard_kernel(const int32_t* __restrict__ tokens, int n,
+                                                                    int vocab, int rows, int off,
+                                                                    const uint16_t* __restrict__ table, int E,
+                                                                    uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * EMB_WAVES + (threadIdx.x >> 6);
+  if (t >= n) return;
+  const int tok = tokens[t];
+  const int local = tok - off;
+  const bool hit = tok >= 0 && tok < vocab && local >= 0 && local < rows;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(table + (int64_t)(hit ? local : 0) * E);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (int64_t)t * E);
+  const int nvec = E / 8;
+  if (hit) {
+    for (int i = lane; i < nvec; i += 64) dst[i] = src[i];
+  } else {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int i = lane; i < nvec; i += 64) dst[i] = z;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_embed_shard(const int32_t* tokens, int n, int vocab, int rows, int off, const uint16_t* table,
+                              int E, uint16_t* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_shard_kernel, dim3((n + EMB_WAVES - 1) / EMB_WAVES), dim3(EMB_WAVES * 64), 0, stream,
+                     tokens, n, vocab, rows, off, table, E, out);
+  return hipGetLastError();
+}
+
+}  // namespace tpk

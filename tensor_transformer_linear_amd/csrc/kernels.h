@@ -65,6 +65,11 @@ int gemm_fp8_pick_tile(int M, int N, int K);
 // q = nearest E4M3 code of x / scale (ties to even, saturating, signed zero). K % 8 == 0.
 hipError_t launch_quantize_rows_e4m3(const uint16_t* x, int M, int K, uint8_t* q, float* scale, hipStream_t stream);
 
+// One rank's embedding rows: out[t] = table[tokens[t] - off] when the id falls in the shard
+// [off, off + rows) and in [0, vocab), else zeros. E % 8 == 0.
+hipError_t launch_embed_shard(const int32_t* tokens, int n, int vocab, int rows, int off, const uint16_t* table,
+                              int E, uint16_t* out, hipStream_t stream);
+
 // RMSNorm statistics: r[m] = rsqrt(mean_k x^2 + eps) for every row, t[k] = bf16(1 + s[k]),
 // and, when xnorm is non-null, the normalised bf16 rows.
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, const uint16_t* scale, float eps, float* r,

@@ -197,6 +197,30 @@ TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M
   return hip_status(tpk::launch_gemm_fp8(p, tile, as_stream(stream)), "tp_column_linear_fp8 launch");
 }
 
+TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,
+                              const void* table_shard, int64_t E, void* out, void* stream) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (n_tokens < 0 || vocab < 1 || E < 1)
+    return fail(TP_ERR_INVALID_ARG, "n_tokens = %lld, vocab = %lld, E = %lld: need n_tokens >= 0, vocab > 0, E > 0",
+                (long long)n_tokens, (long long)vocab, (long long)E);
+  if (table_shard == nullptr || (n_tokens > 0 && (tokens == nullptr || out == nullptr)))
+    return fail(TP_ERR_INVALID_ARG, "tokens, table_shard and out must be non-NULL");
+  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
+  if (n_tokens > INT_MAX || vocab > INT_MAX || E > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (E % 8) return fail(TP_ERR_UNSUPPORTED, "E = %lld must be a multiple of 8", (long long)E);
+  if (!aligned(table_shard, 16) || !aligned(out, 16) || !aligned(tokens, 4))
+    return fail(TP_ERR_UNSUPPORTED, "table_shard and out must be 16-byte aligned, tokens 4-byte aligned");
+  if (n_tokens == 0) return ok();
+  const int64_t rows = width_of(vocab, tp_size, rank);
+  int64_t off = 0;
+  for (int q = 0; q < rank; ++q) off += width_of(vocab, tp_size, q);
+  return hip_status(tpk::launch_embed_shard(tokens, (int)n_tokens, (int)vocab, (int)rows, (int)off,
+                                            static_cast<const uint16_t*>(table_shard), (int)E,
+                                            static_cast<uint16_t*>(out), as_stream(stream)),
+                    "tp_vocab_embedding launch");
+}
+
 TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
                           const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream) {
   if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);

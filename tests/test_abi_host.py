@@ -239,3 +239,24 @@ def test_column_linear_fp8_rejects(kw, status):
 
 def test_column_linear_fp8_empty_input_is_a_no_op():
     assert col8(M=0, x=None, xs=None, y=None) == tt.TP_OK
+
+
+def emb(**kw):
+    a = dict(t=A, n=64, vocab=1000, tp=4, rank=1, tbl=A2, E=128, out=A3)
+    a.update(kw)
+    return L.tp_vocab_embedding(a["t"], a["n"], a["vocab"], a["tp"], a["rank"], a["tbl"], a["E"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(t=None), tt.TP_ERR_INVALID_ARG), (dict(tbl=None), tt.TP_ERR_INVALID_ARG), (dict(out=None), tt.TP_ERR_INVALID_ARG),
+    (dict(n=-1), tt.TP_ERR_INVALID_ARG), (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(rank=4), tt.TP_ERR_INVALID_ARG),
+    (dict(vocab=3), tt.TP_ERR_SHAPE), (dict(E=12), tt.TP_ERR_UNSUPPORTED), (dict(out=MIS), tt.TP_ERR_UNSUPPORTED),
+    (dict(E=0), tt.TP_ERR_INVALID_ARG),
+])
+def test_vocab_embedding_rejects(kw, status):
+    assert emb(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_vocab_embedding_empty_is_a_no_op():
+    assert emb(n=0, t=None, out=None) == tt.TP_OK
