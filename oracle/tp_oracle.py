@@ -542,3 +542,90 @@ def embed_shard(tokens, vocab: int, tp_size: int, rank: int, table_bits):
     out = np.zeros((tok.size, tbl.shape[1]), dtype=np.uint16)
     out[hit] = tbl[local[hit]]
     return out
+
+
+# --------------------------------------------------------------------------------------
+# F2 - fused q_wi projection with SwiGLU, fused o_wo row partial
+#      [palm] _transformer_layer_weight_stationary, transformer_layer_weight_gathered:
+#      the q_wi projection, the SwiGLU step and the o_wo projection
+# --------------------------------------------------------------------------------------
+
+def swish(v) -> np.ndarray:
+    """Swish with unit slope, ``v * sigmoid(v) = v / (1 + exp(-v))``, in float64.
+
+    [palm] forms the MLP activation as ``swish2(wi0) * wi1`` (SwiGLU, at the full d_ff width
+    rather than the 2/3-scaled one).  ``swish2`` is not defined on the page; reading: the Swish
+    of the GLU-variants paper that the page cites, with beta = 1 (SiLU).  For v < -709 the
+    exponential overflows to inf and the quotient is -0, its limit.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def qwi_dims(heads: int, padded_heads: int, qkv: int, ff: int, tp_size: int):
+    """``(h_r, fph, qph)``: heads per rank, MLP columns per head, q_wi columns per head.
+
+    [palm] slices each head's q_wi output into ``qkv`` query columns, then ``wi0`` and ``wi1``
+    of ``ff // (heads - padded_heads)`` columns each: the d_ff width is spread over the real
+    heads, and the padded heads (there so the head axis divides the device mesh) carry the
+    same per-head width.  Heads are split evenly over ranks (reading: ``heads`` includes the
+    padding and must divide by ``tp_size``).
+    """
+    if heads < 1 or not (0 <= padded_heads < heads) or qkv < 1 or ff < 1 or tp_size < 1:
+        raise ValueError("need heads >= 1, 0 <= padded_heads < heads, qkv >= 1, ff >= 1, tp_size >= 1")
+    if heads % tp_size:
+        raise ValueError(f"heads {heads} do not split evenly over {tp_size} ranks")
+    fph = ff // (heads - padded_heads)
+    if fph < 1:
+        raise ValueError("ff is smaller than the number of real heads")
+    return heads // tp_size, fph, qkv + 2 * fph
+
+
+def qwi_swiglu(x_bits, w_qwi_bits, heads: int, padded_heads: int, qkv: int, ff: int, tp_size: int, rank: int):
+    """One rank's fused q_wi projection and the SwiGLU of its MLP columns.
+
+    [palm] q_wi: ``einsum('bte,hed->bthd', xnorm, q_wi)`` over the rank's heads, in the
+    intermediate dtype; ``q = q_wi[..., :qkv]``, ``wi0`` and ``wi1`` the next two ``fph``-wide
+    slices; SwiGLU: ``y_mlp = swish2(wi0) * wi1``.
+
+    ``w_qwi_bits`` is the rank's weight with the per-head output axis first, E contiguous:
+    ``[h_r * qph, E]``, head-major, and within a head ``qkv`` query rows, ``fph`` wi0 rows,
+    ``fph`` wi1 rows (the page's ``[heads, embed, q_wi_per_head]`` shard, transposed once at
+    load).  Per element: ``q_wi = bf16(f32(sum_e x w))``; ``y = bf16(f32(swish(wi0) * wi1))``
+    on the bf16 values of wi0 and wi1 (reading: Swish and the product are evaluated together
+    and rounded once).  Returns ``(q [M, h_r, qkv], y_mlp [M, h_r, fph])`` as bf16 bits.
+    """
+    h_r, fph, qph = qwi_dims(heads, padded_heads, qkv, ff, tp_size)
+    if not 0 <= rank < tp_size:
+        raise ValueError(f"rank {rank} outside [0, {tp_size})")
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_qwi_bits)
+    if w.shape[0] != h_r * qph or w.shape[1] != x.shape[1]:
+        raise ValueError(f"w_qwi is {w.shape}, expected ({h_r * qph}, {x.shape[1]})")
+    qwi = bf16_round(f32(x @ w.T)).reshape(x.shape[0], h_r, qph)
+    q = qwi[:, :, :qkv]
+    wi0 = bf16_to_f64(qwi[:, :, qkv:qkv + fph])
+    wi1 = bf16_to_f64(qwi[:, :, qkv + fph:])
+    y = bf16_round(f32(swish(wi0) * wi1))
+    return np.ascontiguousarray(q), y
+
+
+def fuse_heads(y_att_bits, y_mlp_bits) -> np.ndarray:
+    """[palm] ``y_fused = concatenate([y_att, y_mlp], -1)``: per head, the attention output's
+    ``qkv`` columns, then the MLP's ``fph`` columns: ``[M, h_r, qkv + fph]``."""
+    return np.concatenate([np.asarray(y_att_bits, dtype=np.uint16), np.asarray(y_mlp_bits, dtype=np.uint16)], axis=-1)
+
+
+def o_wo_partial(y_fused_bits, w_o_bits, y_prev=None) -> np.ndarray:
+    """One rank's fused attention-out and MLP-out projection, float32, before any reduction.
+
+    [palm] o_wo: ``einsum('bthd,hde->bte', y_fused, o_wo)`` contracts over the rank's heads
+    and each head's ``qkv + fph`` columns; the page then reduce-scatters the partials over the
+    devices holding the other heads.  ``w_o_bits`` is ``[E, h_r * (qkv + fph)]`` (the page's
+    ``[heads, d, embed]`` shard transposed once at load, so the contraction axis is
+    contiguous).  ``P[m, e] = f32(sum_{h,d} y_fused[m,h,d] o_wo[h,d,e])``; the row-parallel
+    partial with the flattened (head, d) axis as its input width.
+    """
+    yf = np.asarray(y_fused_bits, dtype=np.uint16)
+    return row_linear_partial(yf.reshape(yf.shape[0], -1), w_o_bits, None, rank=0, y_prev=y_prev)
