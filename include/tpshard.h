@@ -29,8 +29,9 @@
  *  [deepspeed] DeepSpeed module_inject/layers.py, class SubParamLinearLayer
  *              (docstring, __init__, forward).
  *  [palm]      google-research scaling_transformer_inference_efficiency
- *              layers/two_d_parallel_xmap.py: allgather_layernorm,
- *              unembed_manual, transformer_layer_weight_gathered.
+ *              layers/two_d_parallel_xmap.py: allgather_layernorm, embed_manual,
+ *              unembed_manual, _transformer_layer_weight_stationary,
+ *              transformer_layer_weight_gathered.
  *  [tt]        Tenstorrent models/common/modules/lm_head/lm_head_1d.py:
  *              module docstring, LMHead1DConfig, LMHead1D.forward,
  *              LMHead1D.from_model_args.
@@ -168,6 +169,51 @@ TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M
  */
 TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,
                               const void* table_shard, int64_t E, void* out, void* stream);
+
+/*
+ * tp_qwi_swiglu - one rank's fused q_wi projection with the SwiGLU of its MLP columns.
+ *
+ * [palm] q_wi and SwiGLU steps of the transformer layers: one product of the normalised
+ * input with each head's q_wi weight gives the head's qkv query columns, then wi0 and wi1
+ * of fph = ff / (heads - padded_heads) columns each (integer division: the d_ff width is
+ * spread over the real heads); the MLP activation is swish(wi0) * wi1 at the full d_ff
+ * width. Heads split evenly over ranks: the rank holds h_r = heads / tp_size of them.
+ * Per output: wi0 and wi1 are float32 accumulators rounded to bf16, then
+ * y = bf16(wi0 / (1 + exp(-wi0)) * wi1) (Swish with unit slope) in float32.
+ *
+ * xnorm     device bf16 [M, E], E % 8 == 0
+ * heads     all heads, padding included (heads % tp_size == 0); 0 <= padded_heads < heads
+ * w_qwi     device bf16 [h_r * (qkv + 2 fph), E]: the rank's heads in order, each head's
+ *           qkv query rows, then its fph wi0 rows, then its fph wi1 rows (the page's
+ *           [heads, E, q_wi_per_head] shard with the output axis first, E contiguous)
+ * q         device bf16 [M, h_r, qkv], or NULL to skip the query columns
+ * y_fused   device bf16 [M, h_r, qkv + fph]: y is written at [m, h, qkv + j]; the
+ *           attention slots [m, h, 0:qkv] are left as they are (the page concatenates the
+ *           attention output there before the o_wo projection)
+ * All pointers 16-byte aligned. M = 0 enqueues nothing. Errors: TP_ERR_INVALID_ARG,
+ * TP_ERR_SHAPE (heads % tp_size, fph < 1), TP_ERR_UNSUPPORTED (E % 8, misalignment,
+ * sizes beyond 31 bits), TP_ERR_HIP.
+ */
+TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv,
+                         int64_t ff, int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream);
+
+/*
+ * tp_o_wo_partial - one rank's fused attention-out and MLP-out projection, before any
+ * reduction.
+ *
+ * [palm] o_wo step: y_out[m, e] = sum over the rank's heads h and each head's qkv + fph
+ * positions d of y_fused[m, h, d] * o_wo[h, d, e], a float32 partial that the page then
+ * reduce-scatters over the devices holding the other heads. Dimensions as tp_qwi_swiglu.
+ *
+ * y_fused    device bf16 [M, h_r, qkv + fph]; h_r (qkv + fph) % 8 == 0
+ * w_o        device bf16 [E, h_r (qkv + fph)] (the page's [heads, d, E] shard transposed,
+ *            the contraction axis contiguous)
+ * y_partial  device f32 [M, E]; accumulate = 1 adds to the values there (one rounding)
+ * Errors: as tp_qwi_swiglu; TP_ERR_UNSUPPORTED when h_r (qkv + fph) % 8 != 0.
+ */
+TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
+                           int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
+                           int accumulate, void* stream);
 
 /*
  * tp_row_linear_partial - one rank's row-parallel partial sum, before any reduction.

@@ -35,6 +35,8 @@ SIGNATURES = {
     "tp_vocab_embedding": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp]),
     "tp_column_linear_fp8": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _P64, _int, _int, _int, _int, _vp, _int,
                                     _int, _i64, _vp]),
+    "tp_qwi_swiglu": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
+    "tp_o_wo_partial": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp]),
     "tp_rmsnorm_workspace_bytes": (_sz, [_i64, _i64]),
     "tp_rmsnorm_workspace_min_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_column_linear": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _P64, _int, _int, _int,
@@ -174,6 +176,29 @@ def tp_row_linear_partial(x_shard, K_logical, w_shard, bias, tp_size, rank, y_pa
         y_partial = torch.empty((M, N), dtype=torch.float32, device=x_shard.device)
     _check(lib().tp_row_linear_partial(_ptr(x_shard), M, K_logical, N, _ptr(w_shard), _ptr(bias), tp_size, rank,
                                        _ptr(y_partial), accumulate, _stream(stream)))
+    return y_partial
+
+
+def tp_qwi_swiglu(xnorm, heads, padded_heads, qkv, ff, tp_size, rank, w_qwi, y_fused, q=None, stream=None):
+    """The rank's fused q_wi projection: SwiGLU of its MLP columns into the MLP slots of
+    ``y_fused`` ``[M, h_r, qkv + fph]`` (attention slots untouched) and, when ``q`` is given,
+    the query columns ``[M, h_r, qkv]``; returns ``(q, y_fused)``."""
+    M, E = xnorm.shape
+    _check(lib().tp_qwi_swiglu(_ptr(xnorm), M, E, heads, padded_heads, qkv, ff, tp_size, rank, _ptr(w_qwi), _ptr(q),
+                               _ptr(y_fused), _stream(stream)))
+    return q, y_fused
+
+
+def tp_o_wo_partial(y_fused, heads, padded_heads, qkv, ff, tp_size, rank, w_o, y_partial=None, accumulate=0,
+                    stream=None):
+    """The rank's float32 partial of the fused attention-out + MLP-out projection
+    ``y_fused [M, h_r (qkv + fph)] @ w_o.T`` with ``w_o [E, h_r (qkv + fph)]``; returns ``y_partial``."""
+    M = y_fused.shape[0]
+    E = w_o.shape[0]
+    if y_partial is None:
+        y_partial = torch.empty((M, E), dtype=torch.float32, device=y_fused.device)
+    _check(lib().tp_o_wo_partial(_ptr(y_fused), M, heads, padded_heads, qkv, ff, E, tp_size, rank, _ptr(w_o),
+                                 _ptr(y_partial), accumulate, _stream(stream)))
     return y_partial
 
 

@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // cancelling in 1 + erf.
 __device__ __forceinline__ float gelu_erf(float a) { return 0.5f * a * erfcf(-a * 0.70710678118654752f); }
 
+// SwiGLU of one output from float32 accumulators: the gate and the value are rounded to bf16
+// first, then Swish with unit slope, g / (1 + exp(-g)), times the value, in float32. For
+// g < -88.7 exp(-g) is inf and the Swish is -0, its limit.
+__device__ __forceinline__ float swiglu_of(float gate, float value) {
+  const float g = bf16_to_f32(f32_to_bf16(gate)), u = bf16_to_f32(f32_to_bf16(value));
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>). Register arrays indexed
 // by these constants stay in registers whatever the unroller decides.
 template <typename F, int... Is>

@@ -52,6 +52,35 @@ __device__ __forceinline__ u32x4_t rms_apply(u32x4_t a, float r, u32x4_t t, bool
   return o;
 }
 
+// Logical output column fed by tile-local B row r of a tile whose first output column is n0.
+// A SwiGLU tile covers BN / 2 output columns: rows [0, BN / 2) are their gates and rows
+// [BN / 2, BN) their values.
+template <int BN>
+__device__ __forceinline__ int tile_b_col(const GemmProblem& p, int n0, int r) {
+  return n0 + (p.ep.glu && r >= BN / 2 ? r - BN / 2 : r);
+}
+
+// B row of tile-local row r (columns past N read the last column's row: their outputs are never
+// stored): the logical column, through the per-head row map, plus the value offset.
+template <int BN>
+__device__ __forceinline__ int tile_b_row(const GemmProblem& p, int n0, int r) {
+  const int c = min(tile_b_col<BN>(p, n0, r), p.N - 1);
+  int row = c;
+  if (p.b_head_w > 0) {
+    const int h = c / p.b_head_w;
+    row = h * p.b_head_pitch + p.b_head_off + (c - h * p.b_head_w);
+  }
+  if (p.ep.glu && r >= BN / 2) row += p.ep.glu_off;
+  return row;
+}
+
+// Output element of logical column c in a row (the per-head placement, if any).
+__device__ __forceinline__ int64_t head_out_col(const GemmEpilogue& ep, int c) {
+  if (ep.c_head_w <= 0) return c;
+  const int h = c / ep.c_head_w;
+  return (int64_t)h * ep.c_head_pitch + ep.c_head_off + (c - h * ep.c_head_w);
+}
+
 // Output stage of a BM x BN tile, one 32-row band of every wave at a time. In a 32x32
 // accumulator block, lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of
 // its sixteen values v. Each wave parks its band (32 rows x WN columns) in LDS; the
@@ -80,6 +109,39 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
       });
     });
     __syncthreads();
+    if (ep.glu) {
+      // SwiGLU: the gate of output column n0 + c is staged at column c, its value at BN / 2 + c
+      constexpr int C8 = BN / 8;
+      constexpr int GCHUNKS = SROWS * C8;
+      static_assert(GCHUNKS % NT == 0, "SwiGLU band chunks must divide evenly over the workgroup");
+      for (int q = 0; q < GCHUNKS / NT; ++q) {
+        const int id = tid + q * NT;
+        const int sr = id / C8, c4 = id - sr * C8;
+        const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+        const int col = n0 + c4 * 4;
+        if (row < M && col < N) {
+          const f32x4_t g = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4);
+          const f32x4_t u = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + BN / 2 + c4 * 4);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = swiglu_of(g[e], u[e]);
+          uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc;
+          const int in_head = ep.c_head_w > 0 ? col % ep.c_head_w : 0;
+          const bool whole = col + 4 <= N && (ep.c_head_w <= 0 || in_head + 4 <= ep.c_head_w);
+          uint16_t* c = out + head_out_col(ep, col);
+          if (whole && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
+            uint2 pk;
+            pk.x = pack_bf16x2(y[0], y[1]);
+            pk.y = pack_bf16x2(y[2], y[3]);
+            *reinterpret_cast<uint2*>(c) = pk;
+          } else {
+            for (int e = 0; e < 4 && col + e < N; ++e) out[head_out_col(ep, col + e)] = f32_to_bf16(y[e]);
+          }
+        }
+      }
+      __syncthreads();
+      return;
+    }
     for (int q = 0; q < CHUNKS / NT; ++q) {
       const int id = tid + q * NT;
       const int sr = id / C4, c4 = id - sr * C4;
@@ -174,7 +236,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
   const int grp = lid / per_group, first_m = grp * group_m;
   const int gsz = min(tiles_m - first_m, group_m);
   const int in = lid - grp * per_group;
-  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * BN;
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (p.ep.glu ? BN / 2 : BN);
 
   const int M = p.M, N = p.N, K = p.K;
   const int kc = tid & 7;          // this thread's 16-byte chunk within a 64-wide K slab
@@ -203,9 +265,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
-    const int gn = n0 + lrow + i * ROWS_PER_PASS;
-    b_ok[i] = gn < N;
-    b_off[i] = (int64_t)(b_ok[i] ? gn : N - 1) * p.ldb + kc * 8;
+    const int r = lrow + i * ROWS_PER_PASS;
+    b_ok[i] = tile_b_col<BN>(p, n0, r) < N;
+    b_off[i] = (int64_t)tile_b_row<BN>(p, n0, r) * p.ldb + kc * 8;
   }
   // One K step's operand pieces in registers.
   struct Regs {
@@ -351,7 +413,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   const int grp = lid / per_group, first_m = grp * group_m;
   const int gsz = min(tiles_m - first_m, group_m);
   const int in = lid - grp * per_group;
-  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * BN;
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (p.ep.glu ? BN / 2 : BN);
   const int M = p.M, N = p.N, K = p.K;
   constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
   const int nk = K / (DROW / ESZ);    // a stage is 64 bytes of every row
@@ -368,7 +430,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       const int gm = min(m0 + row, M - 1);
       src[b] = reinterpret_cast<const unsigned char*>(p.A) + ((int64_t)gm * p.lda) * ESZ + c * 16;
     } else {
-      const int gn = blk < NBLK ? min(n0 + row, N - 1) : 0;
+      const int gn = blk < NBLK ? tile_b_row<BN>(p, n0, row) : 0;
       src[b] = reinterpret_cast<const unsigned char*>(p.B) + ((int64_t)gn * p.ldb) * ESZ + c * 16;
     }
     dst[b] = blk * 1024;
@@ -527,7 +589,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED = 0>
 hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  const int bn_out = p.ep.glu ? BN / 2 : BN;  // output columns per tile
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + bn_out - 1) / bn_out;
   const int nb = tiles_m * tiles_n;
   const int group_m = tiles_m < 4 ? tiles_m : 4;  // 4 M-tiles per group: measured best for L2 reuse
   dim3 grid(nb), block(WAVES_M * WAVES_N * 64);
@@ -586,7 +649,7 @@ int gemm_pick_tile(int M, int N, int K) {
 }
 
 hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream) {
-  if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.N, p.K);
+  if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.ep.glu ? 2 * p.N : p.N, p.K);
   switch (tile) {
     case TILE_256x256: return launch_tile<256, 256, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_256x128: return launch_tile<256, 128, 2, 2, 6>(p, path, stream);

@@ -21,6 +21,14 @@ struct GemmEpilogue {
   int seg_delta[TP_MAX_SUBPARAMS];  // output column minus local column inside the segment
   const float* row_scale;  // f32 [M] or nullptr: acc * row_scale[m] * col_scale[n] before the bias
   const float* col_scale;  // f32 [N] (with row_scale)
+  // SwiGLU (glu = 1): output column c pairs its gate (B row of c) with its value (glu_off B rows
+  // further) and stores bf16(swish(bf16(gate)) * bf16(value)); a tile then covers BN / 2 output
+  // columns. bf16 output only; no bias, activation or scales.
+  int glu;
+  int glu_off;
+  // Optional per-head output placement (c_head_w > 0, used with glu): column c of head
+  // h = c / c_head_w goes to h * c_head_pitch + c_head_off + c % c_head_w.
+  int c_head_w, c_head_pitch, c_head_off;
 };
 
 // C[M,N] = A[M,K] * B[N,K]^T with both operands K-contiguous (weights as stored).
@@ -35,6 +43,9 @@ struct GemmProblem {
   // or bf16(a * row_r[m]) when col_t is null.
   const float* row_r;     // f32 [M] or nullptr (no normalisation)
   const uint16_t* col_t;  // bf16 [K] or nullptr
+  // Optional per-head B rows (b_head_w > 0): column c of head h = c / b_head_w reads B row
+  // h * b_head_pitch + b_head_off + c % b_head_w (a slice of every head's rows).
+  int b_head_w, b_head_pitch, b_head_off;
   GemmEpilogue ep;
 };
 

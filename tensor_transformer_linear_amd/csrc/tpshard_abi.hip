@@ -129,6 +129,35 @@ int prepare_column(const void* x, int64_t M, int64_t K, const void* w_shard, con
   return TP_OK;
 }
 
+// Head dimensions of the fused q_wi / o_wo layers: heads split evenly over ranks, the MLP
+// width spread over the real heads.
+struct HeadDims {
+  int64_t h_r, fph, qph, fused;  // heads per rank, MLP columns per head, q_wi rows per head, y_fused columns per head
+};
+
+int resolve_heads(int64_t heads, int64_t padded_heads, int64_t qkv, int64_t ff, int tp_size, int rank, HeadDims* d) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (heads < 1 || qkv < 1 || ff < 1)
+    return fail(TP_ERR_INVALID_ARG, "heads = %lld, qkv = %lld, ff = %lld must be positive", (long long)heads,
+                (long long)qkv, (long long)ff);
+  if (padded_heads < 0 || padded_heads >= heads)
+    return fail(TP_ERR_INVALID_ARG, "padded_heads = %lld outside [0, heads = %lld)", (long long)padded_heads,
+                (long long)heads);
+  if (heads % tp_size)
+    return fail(TP_ERR_SHAPE, "heads = %lld do not split evenly over tp_size %d", (long long)heads, tp_size);
+  if (heads > INT_MAX || qkv > INT_MAX || ff > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  d->h_r = heads / tp_size;
+  d->fph = ff / (heads - padded_heads);
+  if (d->fph < 1)
+    return fail(TP_ERR_SHAPE, "ff = %lld is smaller than the %lld real heads", (long long)ff,
+                (long long)(heads - padded_heads));
+  d->qph = qkv + 2 * d->fph;
+  d->fused = qkv + d->fph;
+  if (d->h_r * d->qph > INT_MAX / 2) return fail(TP_ERR_UNSUPPORTED, "the rank's q_wi rows must fit in 30 bits");
+  return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +286,90 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
   p.ep.out_f32 = 1;
   p.ep.accumulate = accumulate;
   return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_row_linear_partial launch");
+}
+
+TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv,
+                         int64_t ff, int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream) {
+  HeadDims d;
+  int st = resolve_heads(heads, padded_heads, qkv, ff, tp_size, rank, &d);
+  if (st != TP_OK) return st;
+  if (M < 0 || E < 1) return fail(TP_ERR_INVALID_ARG, "M = %lld, E = %lld: need M >= 0, E > 0", (long long)M, (long long)E);
+  if (w_qwi == nullptr || (M > 0 && (xnorm == nullptr || y_fused == nullptr)))
+    return fail(TP_ERR_INVALID_ARG, "xnorm, w_qwi and y_fused must be non-NULL");
+  if (M > INT_MAX || E > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and E must fit in 31 bits");
+  if (E % 8) return fail(TP_ERR_UNSUPPORTED, "E = %lld must be a multiple of 8", (long long)E);
+  if (!aligned(xnorm, 16) || !aligned(w_qwi, 16) || !aligned(y_fused, 16) || !aligned(q, 16))
+    return fail(TP_ERR_UNSUPPORTED, "xnorm, w_qwi, q and y_fused must be 16-byte aligned");
+  if (M == 0) return ok();
+
+  tpk::GemmProblem p;
+  memset(&p, 0, sizeof(p));
+  p.A = static_cast<const uint16_t*>(xnorm);
+  p.lda = E;
+  p.B = static_cast<const uint16_t*>(w_qwi);
+  p.ldb = E;
+  p.M = (int)M;
+  p.K = (int)E;
+  hipStream_t s = as_stream(stream);
+  // MLP columns: output column c = h * fph + j pairs wi0 row h * qph + qkv + j with the wi1
+  // row fph further and lands at y_fused[m, h, qkv + j].
+  tpk::GemmProblem g = p;
+  g.N = (int)(d.h_r * d.fph);
+  g.b_head_w = (int)d.fph;
+  g.b_head_pitch = (int)d.qph;
+  g.b_head_off = (int)qkv;
+  g.ep.C = y_fused;
+  g.ep.ldc = d.h_r * d.fused;
+  g.ep.glu = 1;
+  g.ep.glu_off = (int)d.fph;
+  g.ep.c_head_w = (int)d.fph;
+  g.ep.c_head_pitch = (int)d.fused;
+  g.ep.c_head_off = (int)qkv;
+  hipError_t e = tpk::launch_gemm(g, g_tile_override, g_path_override, s);
+  if (e != hipSuccess || q == nullptr) return hip_status(e, "tp_qwi_swiglu SwiGLU launch");
+  // Query columns: output column c = h * qkv + t reads row h * qph + t, stored densely.
+  tpk::GemmProblem a = p;
+  a.N = (int)(d.h_r * qkv);
+  a.b_head_w = (int)qkv;
+  a.b_head_pitch = (int)d.qph;
+  a.b_head_off = 0;
+  a.ep.C = q;
+  a.ep.ldc = d.h_r * qkv;
+  return hip_status(tpk::launch_gemm(a, g_tile_override, g_path_override, s), "tp_qwi_swiglu query launch");
+}
+
+TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
+                           int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
+                           int accumulate, void* stream) {
+  HeadDims d;
+  int st = resolve_heads(heads, padded_heads, qkv, ff, tp_size, rank, &d);
+  if (st != TP_OK) return st;
+  if (M < 0 || E < 1) return fail(TP_ERR_INVALID_ARG, "M = %lld, E = %lld: need M >= 0, E > 0", (long long)M, (long long)E);
+  if (w_o == nullptr || (M > 0 && (y_fused == nullptr || y_partial == nullptr)))
+    return fail(TP_ERR_INVALID_ARG, "y_fused, w_o and y_partial must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (M > INT_MAX || E > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and E must fit in 31 bits");
+  const int64_t K = d.h_r * d.fused;
+  if (K % 8)
+    return fail(TP_ERR_UNSUPPORTED, "the rank's y_fused width %lld must be a multiple of 8", (long long)K);
+  if (!aligned(y_fused, 16) || !aligned(w_o, 16) || !aligned(y_partial, 16))
+    return fail(TP_ERR_UNSUPPORTED, "y_fused, w_o and y_partial must be 16-byte aligned");
+  if (M == 0) return ok();
+  tpk::GemmProblem p;
+  memset(&p, 0, sizeof(p));
+  p.A = static_cast<const uint16_t*>(y_fused);
+  p.lda = K;
+  p.B = static_cast<const uint16_t*>(w_o);
+  p.ldb = K;
+  p.M = (int)M;
+  p.N = (int)E;
+  p.K = (int)K;
+  p.ep.C = y_partial;
+  p.ep.ldc = E;
+  p.ep.act = TP_ACT_NONE;
+  p.ep.out_f32 = 1;
+  p.ep.accumulate = accumulate;
+  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_o_wo_partial launch");
 }
 
 TP_API size_t tp_rmsnorm_workspace_min_bytes(int64_t M, int64_t K) {

@@ -260,3 +260,50 @@ def test_vocab_embedding_rejects(kw, status):
 
 def test_vocab_embedding_empty_is_a_no_op():
     assert emb(n=0, t=None, out=None) == tt.TP_OK
+
+
+def qwi(**kw):
+    a = dict(x=A, M=64, E=256, heads=6, padded=1, qkv=32, ff=200, tp=2, rank=1, w=A2, q=A3, y=WS)
+    a.update(kw)
+    return L.tp_qwi_swiglu(a["x"], a["M"], a["E"], a["heads"], a["padded"], a["qkv"], a["ff"], a["tp"], a["rank"],
+                           a["w"], a["q"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), tt.TP_ERR_INVALID_ARG), (dict(w=None), tt.TP_ERR_INVALID_ARG), (dict(y=None), tt.TP_ERR_INVALID_ARG),
+    (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(rank=2), tt.TP_ERR_INVALID_ARG), (dict(heads=0), tt.TP_ERR_INVALID_ARG),
+    (dict(padded=6), tt.TP_ERR_INVALID_ARG), (dict(padded=-1), tt.TP_ERR_INVALID_ARG),
+    (dict(qkv=0), tt.TP_ERR_INVALID_ARG), (dict(ff=0), tt.TP_ERR_INVALID_ARG), (dict(M=-1), tt.TP_ERR_INVALID_ARG),
+    (dict(E=0), tt.TP_ERR_INVALID_ARG), (dict(tp=4, rank=0), tt.TP_ERR_SHAPE), (dict(ff=4), tt.TP_ERR_SHAPE),
+    (dict(E=12), tt.TP_ERR_UNSUPPORTED), (dict(q=MIS), tt.TP_ERR_UNSUPPORTED), (dict(y=MIS), tt.TP_ERR_UNSUPPORTED),
+    (dict(ff=1 << 40), tt.TP_ERR_UNSUPPORTED),
+])
+def test_qwi_swiglu_rejects(kw, status):
+    assert qwi(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_qwi_swiglu_empty_is_a_no_op():
+    assert qwi(M=0, x=None, y=None, q=None) == tt.TP_OK
+
+
+def owo(**kw):
+    # h_r = 3, fph = 40: y_fused width 3 * 72 = 216
+    a = dict(y=A, M=64, heads=6, padded=1, qkv=32, ff=200, E=128, tp=2, rank=0, w=A2, out=A3, acc=0)
+    a.update(kw)
+    return L.tp_o_wo_partial(a["y"], a["M"], a["heads"], a["padded"], a["qkv"], a["ff"], a["E"], a["tp"], a["rank"],
+                             a["w"], a["out"], a["acc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(y=None), tt.TP_ERR_INVALID_ARG), (dict(w=None), tt.TP_ERR_INVALID_ARG), (dict(out=None), tt.TP_ERR_INVALID_ARG),
+    (dict(acc=2), tt.TP_ERR_INVALID_ARG), (dict(E=0), tt.TP_ERR_INVALID_ARG), (dict(rank=-1), tt.TP_ERR_INVALID_ARG),
+    (dict(heads=7), tt.TP_ERR_SHAPE), (dict(qkv=33), tt.TP_ERR_UNSUPPORTED), (dict(out=MIS), tt.TP_ERR_UNSUPPORTED),
+])
+def test_o_wo_partial_rejects(kw, status):
+    assert owo(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_o_wo_partial_empty_is_a_no_op():
+    assert owo(M=0, y=None, out=None) == tt.TP_OK
