@@ -45,8 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 = skip)")
     ap.add_argument("--parts", default="1,2,3,4,5", help="comma list of workload parts to run")
-    ap.add_argument("--fp8", type=int, default=1,
-                    help="1: also time the next-row legs, the fp8 prefill column linear and the embedding (0 = skip)")
+    ap.add_argument("--next", "--fp8", dest="next", type=int, default=1,
+                    help="1: also time the legs beyond the five workloads: the fp8 prefill column linear, the "
+                         "fused q_wi + SwiGLU and o_wo projections, and the embedding (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
@@ -357,6 +358,61 @@ def fp8_prefill_leg(launches, stream):
             "end_to_end_tflops": round(flops / ((q_us + g_us) * 1e-6) / 1e12, 1), "launches_timed": launches}
 
 
+def swiglu_leg(launches, stream):
+    """The fused q_wi projection with its SwiGLU and the fused o_wo partial, one rank's share of a
+    PaLM-style layer: 8192 tokens, E 8192, 64 heads of 128, d_ff 32768 spread over the heads
+    (512 per head), tp 8 rank 0 (8 heads): q_wi W [8 x 1152, 8192], o_wo W [8192, 8 x 640].
+    Each entry point is timed with HIP events on the stream it runs on."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    M, E, heads, padded, qkv, ff, tp, rank = 8192, 8192, 64, 0, 128, 32768, 8, 0
+    h_r, fph = heads // tp, ff // (heads - padded)
+    qph, fused = qkv + 2 * fph, qkv + fph
+    dev = torch.device("cuda:0")
+
+    def normal(shape, std, tid):
+        return torch.from_numpy(synth.bf16_normal(shape, std, 12, tid).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = normal((M, E), 1.0, 0)
+    w = normal((h_r * qph, E), 0.02, 1)
+    w_o = normal((E, h_r * fused), 0.02, 2)
+    yf = normal((M, h_r, fused), 1.0, 3)  # attention slots hold a synthetic attention output
+    q = torch.empty((M, h_r, qkv), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, E), dtype=torch.float32, device=dev)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tt.tp_qwi_swiglu(x, heads, padded, qkv, ff, tp, rank, w, yf, q=q)
+        if ev is not None:
+            ev[1].record(stream)
+        tt.tp_o_wo_partial(yf.view(M, -1), heads, padded, qkv, ff, tp, rank, w_o, out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    run()
+    run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        run(ev)
+    torch.cuda.synchronize()
+    a_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    o_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    a_fl = 2.0 * M * E * h_r * qph
+    o_fl = 2.0 * M * E * h_r * fused
+    a_tf, o_tf = a_fl / (a_us * 1e-6) / 1e12, o_fl / (o_us * 1e-6) / 1e12
+    return {"workload": "fused q_wi + SwiGLU and o_wo, 8192 tokens, E 8192, 64 heads x 128, d_ff 32768, tp 8 rank 0",
+            "qwi_swiglu_mean_us": round(a_us, 2), "qwi_swiglu_tflops": round(a_tf, 1),
+            "qwi_swiglu_frac_bf16_peak": round(a_tf / PEAK_BF16_TFLOPS, 4),
+            "o_wo_mean_us": round(o_us, 2), "o_wo_tflops": round(o_tf, 1),
+            "o_wo_frac_bf16_peak": round(o_tf / PEAK_BF16_TFLOPS, 4),
+            "layer_tflops": round((a_fl + o_fl) / ((a_us + o_us) * 1e-6) / 1e12, 1), "launches_timed": launches}
+
+
 def embedding_leg(launches, stream):
     """The vocab-parallel embedding (one rank's share) at the RMSNorm workload's prefill size:
     32768 token ids uniform over a 128256-token vocabulary, tp 8 rank 0 (16032 table rows of
@@ -489,8 +545,9 @@ def main():
 
     value = gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
     roofline = roofline_leg(wl, args.steps, stream) if gemm_ms > 0 else None
-    fp8 = fp8_prefill_leg(args.steps, stream) if args.fp8 else None
-    emb = embedding_leg(args.steps, stream) if args.fp8 else None
+    fp8 = fp8_prefill_leg(args.steps, stream) if args.next else None
+    glu = swiglu_leg(args.steps, stream) if args.next else None
+    emb = embedding_leg(args.steps, stream) if args.next else None
     out = {
         "metric": METRIC, "value": round(value, 2) if value else None, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -504,6 +561,7 @@ def main():
         "roofline": roofline,
         "lm_head": lm or None,
         "fp8_prefill": fp8,
+        "swiglu": glu,
         "embedding": emb,
         "per_config": per_config,
     }

@@ -54,17 +54,20 @@ __device__ __forceinline__ u32x4_t rms_apply(u32x4_t a, float r, u32x4_t t, bool
 
 // Logical output column fed by tile-local B row r of a tile whose first output column is n0.
 // A SwiGLU tile covers BN / 2 output columns: rows [0, BN / 2) are their gates and rows
-// [BN / 2, BN) their values.
-template <int BN>
+// [BN / 2, BN) their values. MAPPED = false compiles the plain kernels (row c for column c, no
+// SwiGLU), so the per-head map costs them nothing.
+template <int BN, bool MAPPED>
 __device__ __forceinline__ int tile_b_col(const GemmProblem& p, int n0, int r) {
+  if constexpr (!MAPPED) return n0 + r;
   return n0 + (p.ep.glu && r >= BN / 2 ? r - BN / 2 : r);
 }
 
 // B row of tile-local row r (columns past N read the last column's row: their outputs are never
 // stored): the logical column, through the per-head row map, plus the value offset.
-template <int BN>
+template <int BN, bool MAPPED>
 __device__ __forceinline__ int tile_b_row(const GemmProblem& p, int n0, int r) {
-  const int c = min(tile_b_col<BN>(p, n0, r), p.N - 1);
+  const int c = min(tile_b_col<BN, MAPPED>(p, n0, r), p.N - 1);
+  if constexpr (!MAPPED) return c;
   int row = c;
   if (p.b_head_w > 0) {
     const int h = c / p.b_head_w;
@@ -87,7 +90,7 @@ __device__ __forceinline__ int64_t head_out_col(const GemmEpilogue& ep, int c) {
 // workgroup then reads the staged band back four consecutive columns per thread and
 // finishes them: bias, GELU, one rounding, the column remap, and a coalesced store (or a
 // float32 add). `smem` must hold WAVES_M * 32 * (BN + 4) floats and be free.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool MAPPED>
 __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (&acc)[FM][FN], unsigned char* smem,
                                                 int m0, int n0, int wm, int wn, int lane, int tid) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -109,7 +112,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
       });
     });
     __syncthreads();
-    if (ep.glu) {
+    if (MAPPED && ep.glu) {
       // SwiGLU: the gate of output column n0 + c is staged at column c, its value at BN / 2 + c
       constexpr int C8 = BN / 8;
       constexpr int GCHUNKS = SROWS * C8;
@@ -213,7 +216,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   });
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool NORM>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool NORM, bool MAPPED>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                         int group_m) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
   const int grp = lid / per_group, first_m = grp * group_m;
   const int gsz = min(tiles_m - first_m, group_m);
   const int in = lid - grp * per_group;
-  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (p.ep.glu ? BN / 2 : BN);
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (MAPPED && p.ep.glu ? BN / 2 : BN);
 
   const int M = p.M, N = p.N, K = p.K;
   const int kc = tid & 7;          // this thread's 16-byte chunk within a 64-wide K slab
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int r = lrow + i * ROWS_PER_PASS;
-    b_ok[i] = tile_b_col<BN>(p, n0, r) < N;
-    b_off[i] = (int64_t)tile_b_row<BN>(p, n0, r) * p.ldb + kc * 8;
+    b_ok[i] = tile_b_col<BN, MAPPED>(p, n0, r) < N;
+    b_off[i] = (int64_t)tile_b_row<BN, MAPPED>(p, n0, r) * p.ldb + kc * 8;
   }
   // One K step's operand pieces in registers.
   struct Regs {
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_kernel(GemmProb
   }
 
   static_assert(WAVES_M * 32 * (BN + 4) * 4 <= 2 * STAGE, "band staging must fit in the pipeline's LDS");
-  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 
@@ -387,7 +390,7 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 // of 32) and one v_mfma_f32_32x32x64_f8f6f4 per 32x32 block takes the place of the two bf16
 // MFMAs: lane l supplies 32 consecutive K bytes (chunks 2 (l / 32) and 2 (l / 32) + 1 of the
 // row), the same for A and B. Only the ping-pong schedule handles it.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED, bool FP8 = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED, bool FP8 = false, bool MAPPED = false>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                                             int group_m) {
   static_assert(!FP8 || SCHED == 1, "the fp8 path runs the ping-pong schedule");
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   const int grp = lid / per_group, first_m = grp * group_m;
   const int gsz = min(tiles_m - first_m, group_m);
   const int in = lid - grp * per_group;
-  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (p.ep.glu ? BN / 2 : BN);
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (MAPPED && p.ep.glu ? BN / 2 : BN);
   const int M = p.M, N = p.N, K = p.K;
   constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
   const int nk = K / (DROW / ESZ);    // a stage is 64 bytes of every row
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       const int gm = min(m0 + row, M - 1);
       src[b] = reinterpret_cast<const unsigned char*>(p.A) + ((int64_t)gm * p.lda) * ESZ + c * 16;
     } else {
-      const int gn = blk < NBLK ? tile_b_row<BN>(p, n0, row) : 0;
+      const int gn = blk < NBLK ? tile_b_row<BN, MAPPED>(p, n0, row) : 0;
       src[b] = reinterpret_cast<const unsigned char*>(p.B) + ((int64_t)gn * p.ldb) * ESZ + c * 16;
     }
     dst[b] = blk * 1024;
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+    gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
     return;
   }
 
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
   }
 }
 
@@ -596,15 +599,26 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   dim3 grid(nb), block(WAVES_M * WAVES_N * 64);
   const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
   if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
-  if (dma_ok && path != GEMM_PATH_REGISTER)
-    hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, SCHED>), grid, block, 0, stream, p, tiles_m,
+  // the per-head row map and SwiGLU run in their own instantiations (never with RMSNorm staging)
+  const bool mapped = p.ep.glu || p.b_head_w > 0;
+  if (mapped && p.row_r != nullptr) return hipErrorInvalidValue;
+  if (dma_ok && path != GEMM_PATH_REGISTER) {
+    if (mapped)
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, SCHED, false, true>), grid, block, 0,
+                         stream, p, tiles_m, tiles_n, group_m);
+    else
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, SCHED>), grid, block, 0, stream, p,
+                         tiles_m, tiles_n, group_m);
+  } else if (p.row_r != nullptr) {
+    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true, false>), grid, block, 0, stream, p, tiles_m,
                        tiles_n, group_m);
-  else if (p.row_r != nullptr)
-    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
-                       group_m);
-  else
-    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, false>), grid, block, 0, stream, p, tiles_m,
+  } else if (mapped) {
+    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, false, true>), grid, block, 0, stream, p, tiles_m,
                        tiles_n, group_m);
+  } else {
+    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WAVES_M, WAVES_N, false, false>), grid, block, 0, stream, p, tiles_m,
+                       tiles_n, group_m);
+  }
   return hipGetLastError();
 }
 
@@ -626,7 +640,9 @@ int gemm_fp8_pick_tile(int M, int N, int K) {
 }
 
 hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
-  if (!p.fp8 || p.K % 64 != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0 || p.row_r != nullptr) return hipErrorInvalidValue;
+  if (!p.fp8 || p.K % 64 != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0 || p.row_r != nullptr || p.ep.glu ||
+      p.b_head_w > 0)
+    return hipErrorInvalidValue;
   if (tile == TILE_AUTO) tile = gemm_fp8_pick_tile(p.M, p.N, p.K);
   switch (tile) {
     case TILE_256x256: return launch_tile_fp8<256, 256>(p, stream);
