@@ -629,3 +629,47 @@ def o_wo_partial(y_fused_bits, w_o_bits, y_prev=None) -> np.ndarray:
     """
     yf = np.asarray(y_fused_bits, dtype=np.uint16)
     return row_linear_partial(yf.reshape(yf.shape[0], -1), w_o_bits, None, rank=0, y_prev=y_prev)
+
+
+# --------------------------------------------------------------------------------------
+# F3 - sequence-parallel reduce-scatter of row partials, residual add
+#      [nanotron] MLP Module (c_proj output [batch, seq // tp, hidden]);
+#      [palm] o_wo step (psum_scatter of the partials) and residual step
+# --------------------------------------------------------------------------------------
+
+def seq_slice_rows(batch: int, seq: int, tp_size: int, dest: int) -> np.ndarray:
+    """Token rows (of the ``[batch * seq]`` axis) that rank ``dest`` holds after a
+    sequence-parallel scatter: positions ``[dest * sl, (dest + 1) * sl)`` of every sequence,
+    ``sl = seq // tp_size``, in batch-major order.
+
+    [nanotron] the row-parallel ``c_proj`` returns ``[batch_size, seq_length // tp_size,
+    hidden_size]``; [palm] scatters the reduced output along the sequence axis in tiles.
+    Reading: ``seq`` must divide by ``tp_size`` (the page's ``seq_length // tp_size`` with no
+    remainder).
+    """
+    if tp_size < 1 or not 0 <= dest < tp_size:
+        raise ValueError("need tp_size >= 1 and 0 <= dest < tp_size")
+    if seq < 1 or seq % tp_size:
+        raise ValueError(f"seq {seq} does not split evenly over {tp_size} ranks")
+    sl = seq // tp_size
+    return (np.arange(batch)[:, None] * seq + dest * sl + np.arange(sl)[None, :]).reshape(-1)
+
+
+def reduce_scatter_residual(partials, batch: int, seq: int, dest: int, residual_bits=None):
+    """Rank ``dest``'s output of the reduce-scatter of the ranks' row partials, plus the residual.
+
+    ``partials[r]`` is rank r's float32 partial ``[batch * seq, N]`` (``row_linear_partial`` or
+    ``o_wo_partial``).  ``S = f32(f32(P_0 + P_1) + ...)`` over the rows of ``dest``'s sequence
+    slice (reading: the sum runs in rank order in float32, the plainest fixed order for the
+    collective the pages leave unspecified); ``z = bf16(f32(S + x))`` with the bf16 residual
+    ``x`` of the slice (``[batch * sl, N]``), [palm] ``z = intermediate_dtype(y_out + x)``.
+    Returns ``(S, z)``; ``z`` is None without a residual.
+    """
+    rows = seq_slice_rows(batch, seq, len(partials), dest)
+    S = rank_ordered_sum([np.asarray(p, dtype=np.float32)[rows] for p in partials])
+    if residual_bits is None:
+        return S, None
+    r = bf16_to_f64(residual_bits)
+    if r.shape != S.shape:
+        raise ValueError(f"residual is {r.shape}, the slice is {S.shape}")
+    return S, bf16_round(f32(S.astype(np.float64) + r))
