@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--parts", default="1,2,3,4,5", help="comma list of workload parts to run")
     ap.add_argument("--next", "--fp8", dest="next", type=int, default=1,
                     help="1: also time the legs beyond the five workloads: the fp8 prefill column linear, the "
-                         "fused q_wi + SwiGLU and o_wo projections, and the embedding (0 = skip)")
+                         "fused q_wi + SwiGLU and o_wo projections, the embedding and the sequence-parallel "
+                         "reduce-scatter with residual (0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
@@ -413,6 +414,46 @@ def swiglu_leg(launches, stream):
             "layer_tflops": round((a_fl + o_fl) / ((a_us + o_us) * 1e-6) / 1e12, 1), "launches_timed": launches}
 
 
+def reduce_scatter_leg(launches, stream):
+    """The sequence-parallel reduce-scatter of the c_proj partials with the residual add, for the
+    llama-8B MLP shard (batch 8, seq 1024, hidden 4096, tp 8): the eight ranks' float32 partials
+    [8192, 4096] summed in rank order over each destination's 1024-row slice, plus a bf16 residual,
+    bf16 out. One launch per destination rank; every rank is timed with HIP events on its stream."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    batch, seq, tp, N = 8, 1024, 8, 4096
+    M, rows = batch * seq, batch * seq // tp
+    dev = torch.device("cuda:0")
+    parts = [torch.from_numpy(synth.rng(13, r).standard_normal((M, N), dtype=np.float32)).to(dev) for r in range(tp)]
+    res = [torch.from_numpy(synth.bf16_normal((rows, N), 1.0, 13, 100 + d).view(np.int16)).view(torch.bfloat16).to(dev)
+           for d in range(tp)]
+    z = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    for d in range(tp):
+        tt.tp_reduce_scatter_residual(parts, batch, seq, d, residual=res[d], z=z)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(tp)]
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        for d in range(tp):
+            ev[d][0].record(stream)
+            tt.tp_reduce_scatter_residual(parts, batch, seq, d, residual=res[d], z=z)
+            ev[d][1].record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) * 1e3 for ev in evs for a, b in ev]
+    us = float(np.median(t))
+    nbytes = tp * rows * N * 4 + rows * N * 2 + rows * N * 2  # partial slices, residual, z
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "sequence-parallel reduce-scatter + residual, llama-8B MLP shard: 8 partials [8192, 4096] f32, "
+                        "tp 8, one destination rank per launch",
+            "median_us": round(us, 2), "mean_us": round(float(np.mean(t)), 2), "bytes_per_launch": nbytes,
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "launches_timed": launches * tp,
+            "timing": "per-launch HIP events; throughput from the median (a ~25 us kernel: one host pause "
+                      "between an event and its launch shows up in that pair)"}
+
+
 def embedding_leg(launches, stream):
     """The vocab-parallel embedding (one rank's share) at the RMSNorm workload's prefill size:
     32768 token ids uniform over a 128256-token vocabulary, tp 8 rank 0 (16032 table rows of
@@ -438,12 +479,14 @@ def embedding_leg(launches, stream):
         tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
         b.record(stream)
     torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    t = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    us = float(np.median(t))
     nbytes = hits * E * 2 + n * 4 + n * E * 2
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"workload": "vocab-parallel embedding, 32768 tokens, E 8192, vocab 128256, tp 8 rank 0",
-            "mean_us": round(us, 2), "bytes": nbytes, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "rows_read": hits, "launches_timed": launches}
+            "median_us": round(us, 2), "mean_us": round(float(np.mean(t)), 2), "bytes": nbytes, "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "rows_read": hits, "launches_timed": launches,
+            "timing": "per-launch HIP events; throughput from the median"}
 
 
 def copy_probe(mb: int):
@@ -548,6 +591,7 @@ def main():
     fp8 = fp8_prefill_leg(args.steps, stream) if args.next else None
     glu = swiglu_leg(args.steps, stream) if args.next else None
     emb = embedding_leg(args.steps, stream) if args.next else None
+    rsc = reduce_scatter_leg(args.steps, stream) if args.next else None
     out = {
         "metric": METRIC, "value": round(value, 2) if value else None, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 4),
@@ -563,6 +607,7 @@ def main():
         "fp8_prefill": fp8,
         "swiglu": glu,
         "embedding": emb,
+        "reduce_scatter": rsc,
         "per_config": per_config,
     }
     if args.cpu_seconds > 0:

@@ -67,6 +67,7 @@ typedef enum { TP_LAYOUT_LOCAL = 0, TP_LAYOUT_LOGICAL = 1 } tp_layout;
 
 /* Largest number of sub-parameters one column-parallel weight may hold. */
 #define TP_MAX_SUBPARAMS 16
+#define TP_MAX_RANKS 64 /* most ranks tp_reduce_scatter_residual sums */
 
 /*
  * tp_shard_widths - the rows of each sub-parameter that rank `rank` owns.
@@ -214,6 +215,30 @@ TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads,
 TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
                            int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
                            int accumulate, void* stream);
+
+/*
+ * tp_reduce_scatter_residual - one rank's output of the sequence-parallel reduce-scatter of
+ * the ranks' row-parallel partials, with the residual add (all ranks' partials on one GPU).
+ *
+ * [nanotron] MLP Module: c_proj, a row-parallel linear, returns [batch, seq / tp, hidden] on
+ * each rank; [palm] reduce-scatters the o_wo partials, then adds the residual,
+ * z = bf16(y_out + x). Rank dest_rank keeps positions [dest_rank sl, (dest_rank + 1) sl) of
+ * every sequence, sl = seq / tp_size. Output row i = b sl + t sums, in rank order and in
+ * float32, row b seq + dest_rank sl + t of every partial: S = ((P_0 + P_1) + ...) + P_tp-1.
+ *
+ * partials   host array of tp_size device pointers, rank r's f32 partial [batch seq, N]
+ *            (tp_row_linear_partial, tp_o_wo_partial); read before the call returns
+ * tp_size    1..TP_MAX_RANKS; seq % tp_size == 0; N % 4 == 0
+ * residual   device bf16 [batch sl, N] (the rank's slice of the residual stream) or NULL
+ * z          device bf16 [batch sl, N]: bf16(S + residual) (bf16(S) without one), or NULL
+ * y_sum      device f32 [batch sl, N]: S, or NULL; z and y_sum are not both NULL when batch > 0
+ * All device pointers 16-byte aligned. batch = 0 enqueues nothing. Errors:
+ * TP_ERR_INVALID_ARG, TP_ERR_SHAPE (seq % tp_size), TP_ERR_UNSUPPORTED (N % 4, misalignment),
+ * TP_ERR_HIP.
+ */
+TP_API int tp_reduce_scatter_residual(const float* const* partials, int tp_size, int64_t batch, int64_t seq,
+                                      int64_t N, int dest_rank, const void* residual, void* z, float* y_sum,
+                                      void* stream);
 
 /*
  * tp_row_linear_partial - one rank's row-parallel partial sum, before any reduction.

@@ -37,6 +37,7 @@ SIGNATURES = {
                                     _int, _i64, _vp]),
     "tp_qwi_swiglu": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp]),
     "tp_o_wo_partial": (_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp]),
+    "tp_reduce_scatter_residual": (_int, [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "tp_rmsnorm_workspace_bytes": (_sz, [_i64, _i64]),
     "tp_rmsnorm_workspace_min_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_column_linear": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _P64, _int, _int, _int,
@@ -200,6 +201,19 @@ def tp_o_wo_partial(y_fused, heads, padded_heads, qkv, ff, tp_size, rank, w_o, y
     _check(lib().tp_o_wo_partial(_ptr(y_fused), M, heads, padded_heads, qkv, ff, E, tp_size, rank, _ptr(w_o),
                                  _ptr(y_partial), accumulate, _stream(stream)))
     return y_partial
+
+
+def tp_reduce_scatter_residual(partials, batch, seq, dest_rank, residual=None, z=None, y_sum=None, stream=None):
+    """Rank ``dest_rank``'s rows of the sequence-parallel reduce-scatter of the float32
+    ``partials`` (one ``[batch * seq, N]`` tensor per rank), summed in rank order, plus the bf16
+    ``residual``: fills ``z`` (bf16) and/or ``y_sum`` (f32), ``[batch * seq / tp, N]``; returns
+    ``(z, y_sum)``."""
+    tp = len(partials)
+    N = partials[0].shape[-1]
+    ptrs = (ctypes.c_void_p * max(1, tp))(*[p.data_ptr() for p in partials])
+    _check(lib().tp_reduce_scatter_residual(ctypes.cast(ptrs, ctypes.c_void_p), tp, batch, seq, N, dest_rank,
+                                            _ptr(residual), _ptr(z), _ptr(y_sum), _stream(stream)))
+    return z, y_sum
 
 
 def tp_rmsnorm_workspace_bytes(M: int, K: int) -> int:

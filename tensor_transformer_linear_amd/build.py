@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
-SOURCES = ["tpshard_abi.hip", "gemm.hip", "rmsnorm.hip", "lm_head.hip", "quant.hip", "embed.hip"]
+SOURCES = ["tpshard_abi.hip", "gemm.hip", "rmsnorm.hip", "lm_head.hip", "quant.hip", "embed.hip", "reduce.hip"]
 ARCH = "gfx950"
 
 

@@ -81,6 +81,21 @@ hipError_t launch_quantize_rows_e4m3(const uint16_t* x, int M, int K, uint8_t* q
 hipError_t launch_embed_shard(const int32_t* tokens, int n, int vocab, int rows, int off, const uint16_t* table,
                               int E, uint16_t* out, hipStream_t stream);
 
+// One destination rank's sequence-parallel reduce-scatter of the ranks' float32 partials
+// [batch * seq, N]: for output row i = b * sl + t (source row b * seq + dest * sl + t),
+// S = rank-ordered float32 sum; y_sum = S and/or z = bf16(S + residual) (residual may be null).
+// N % 4 == 0; every pointer 16-byte aligned.
+struct ReduceScatterProblem {
+  const float* part[TP_MAX_RANKS];
+  int tp, dest;
+  int64_t seq, sl, N;
+  int64_t chunks;  // output rows * N / 4
+  const uint16_t* residual;
+  uint16_t* z;
+  float* y_sum;
+};
+hipError_t launch_reduce_scatter(const ReduceScatterProblem& p, hipStream_t stream);
+
 // RMSNorm statistics: r[m] = rsqrt(mean_k x^2 + eps) for every row, t[k] = bf16(1 + s[k]),
 // and, when xnorm is non-null, the normalised bf16 rows.
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int M, int K, const uint16_t* scale, float eps, float* r,

@@ -372,6 +372,44 @@ TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_
   return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_o_wo_partial launch");
 }
 
+TP_API int tp_reduce_scatter_residual(const float* const* partials, int tp_size, int64_t batch, int64_t seq,
+                                      int64_t N, int dest_rank, const void* residual, void* z, float* y_sum,
+                                      void* stream) {
+  if (tp_size < 1 || tp_size > TP_MAX_RANKS)
+    return fail(TP_ERR_INVALID_ARG, "tp_size = %d outside [1, %d]", tp_size, TP_MAX_RANKS);
+  if (dest_rank < 0 || dest_rank >= tp_size)
+    return fail(TP_ERR_INVALID_ARG, "dest_rank %d outside [0, %d)", dest_rank, tp_size);
+  if (batch < 0 || seq < 1 || N < 1)
+    return fail(TP_ERR_INVALID_ARG, "batch = %lld, seq = %lld, N = %lld: need batch >= 0, seq > 0, N > 0",
+                (long long)batch, (long long)seq, (long long)N);
+  if (partials == nullptr) return fail(TP_ERR_INVALID_ARG, "partials is NULL");
+  if (batch > 0 && z == nullptr && y_sum == nullptr) return fail(TP_ERR_INVALID_ARG, "z and y_sum are both NULL");
+  if (seq % tp_size)
+    return fail(TP_ERR_SHAPE, "seq = %lld does not split evenly over tp_size %d", (long long)seq, tp_size);
+  if (N % 4) return fail(TP_ERR_UNSUPPORTED, "N = %lld must be a multiple of 4", (long long)N);
+  if (batch > INT_MAX || seq > INT_MAX || N > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  for (int r = 0; r < tp_size; ++r) {
+    if (partials[r] == nullptr && batch > 0) return fail(TP_ERR_INVALID_ARG, "partials[%d] is NULL", r);
+    if (!aligned(partials[r], 16)) return fail(TP_ERR_UNSUPPORTED, "partials[%d] must be 16-byte aligned", r);
+  }
+  if (!aligned(residual, 16) || !aligned(z, 16) || !aligned(y_sum, 16))
+    return fail(TP_ERR_UNSUPPORTED, "residual, z and y_sum must be 16-byte aligned");
+  if (batch == 0) return ok();
+  tpk::ReduceScatterProblem p;
+  memset(&p, 0, sizeof(p));
+  for (int r = 0; r < tp_size; ++r) p.part[r] = partials[r];
+  p.tp = tp_size;
+  p.dest = dest_rank;
+  p.seq = seq;
+  p.sl = seq / tp_size;
+  p.N = N;
+  p.chunks = batch * p.sl * (N / 4);
+  p.residual = static_cast<const uint16_t*>(residual);
+  p.z = static_cast<uint16_t*>(z);
+  p.y_sum = y_sum;
+  return hip_status(tpk::launch_reduce_scatter(p, as_stream(stream)), "tp_reduce_scatter_residual launch");
+}
+
 TP_API size_t tp_rmsnorm_workspace_min_bytes(int64_t M, int64_t K) {
   if (M < 0 || K < 0) return 0;
   return align_up((size_t)M * sizeof(float), 256) + align_up((size_t)K * sizeof(uint16_t), 256);

@@ -307,3 +307,31 @@ def test_o_wo_partial_rejects(kw, status):
 
 def test_o_wo_partial_empty_is_a_no_op():
     assert owo(M=0, y=None, out=None) == tt.TP_OK
+
+
+def rs(**kw):
+    a = dict(parts=[A, A2, A3, WS], tp=None, batch=2, seq=8, N=64, dest=1, res=A, z=A2, ys=A3)
+    a.update(kw)
+    parts = a["parts"]
+    tp = (4 if parts is None else len(parts)) if a["tp"] is None else a["tp"]
+    arr = None if parts is None else ctypes.cast((ctypes.c_void_p * max(1, len(parts)))(*parts), ctypes.c_void_p)
+    return L.tp_reduce_scatter_residual(arr, tp, a["batch"], a["seq"], a["N"], a["dest"], a["res"], a["z"], a["ys"],
+                                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(parts=None), tt.TP_ERR_INVALID_ARG), (dict(tp=0), tt.TP_ERR_INVALID_ARG), (dict(tp=65), tt.TP_ERR_INVALID_ARG),
+    (dict(dest=4), tt.TP_ERR_INVALID_ARG), (dict(dest=-1), tt.TP_ERR_INVALID_ARG), (dict(batch=-1), tt.TP_ERR_INVALID_ARG),
+    (dict(seq=0), tt.TP_ERR_INVALID_ARG), (dict(N=0), tt.TP_ERR_INVALID_ARG), (dict(z=None, ys=None), tt.TP_ERR_INVALID_ARG),
+    (dict(parts=[A, None, A3, WS]), tt.TP_ERR_INVALID_ARG), (dict(seq=10), tt.TP_ERR_SHAPE),
+    (dict(N=66), tt.TP_ERR_UNSUPPORTED), (dict(parts=[A, MIS, A3, WS]), tt.TP_ERR_UNSUPPORTED),
+    (dict(z=MIS), tt.TP_ERR_UNSUPPORTED), (dict(res=MIS), tt.TP_ERR_UNSUPPORTED),
+])
+def test_reduce_scatter_rejects(kw, status):
+    assert rs(**kw) == status
+    assert L.tp_last_error().decode() != ""
+
+
+def test_reduce_scatter_empty_batch_is_a_no_op():
+    assert rs(batch=0) == tt.TP_OK
+    assert rs(batch=0, parts=[None, None, None, None], z=None, ys=None, res=None) == tt.TP_OK
