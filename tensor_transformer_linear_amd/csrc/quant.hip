@@ -9,6 +9,13 @@
 //
 // One workgroup per row. Rows up to 8192 wide stay in registers between the amax pass and
 // the encoding pass, so x is read once; wider rows are read a second time (from cache).
+//
+// Rows with a finite maximum encode with gfx950's packed float32 -> E4M3 conversion (two codes
+// per instruction), after clamping the quotient to +-448: on every finite value up to 464 in
+// magnitude that conversion rounds exactly as the definition above (nearest, ties to the even
+// mantissa, subnormal codes, signed zero), and the clamp gives the saturated code beyond. Rows
+// holding an infinity or NaN keep the integer encoder below (every such value saturates).
+
 #include "common.h"
 #include "kernels.h"
 
@@ -89,7 +96,24 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_rows_e4m3_kernel(const uin
   if (tid == 0) scale[row] = s;
 
   // pass 2: codes, eight per 8-byte store
+  const bool finite_row = m < 0x7F800000u;
   auto encode = [&](const u32x4_t& c, int chunk) {
+    if (finite_row) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] = __fdiv_rn(__uint_as_float(c[i] << 16), s);
+        y[2 * i + 1] = __fdiv_rn(__uint_as_float(c[i] & 0xFFFF0000u), s);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_fmed3f(y[e], -448.0f, 448.0f);
+      uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+      *reinterpret_cast<uint2*>(qr + chunk * 8) = make_uint2(lo, hi);
+      return;
+    }
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
