@@ -395,6 +395,9 @@ TP_API int tp_reduce_scatter_residual(const float* const* partials, int tp_size,
   if (!aligned(residual, 16) || !aligned(z, 16) || !aligned(y_sum, 16))
     return fail(TP_ERR_UNSUPPORTED, "residual, z and y_sum must be 16-byte aligned");
   if (batch == 0) return ok();
+  // one thread per four outputs in a 1-D grid of 256-thread workgroups (checked without overflow)
+  if (batch * (seq / tp_size) > (int64_t)INT_MAX * 256 / (N / 4))
+    return fail(TP_ERR_UNSUPPORTED, "batch * seq / tp_size * N is too large for one launch");
   tpk::ReduceScatterProblem p;
   memset(&p, 0, sizeof(p));
   for (int r = 0; r < tp_size; ++r) p.part[r] = partials[r];

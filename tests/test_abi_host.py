@@ -332,6 +332,10 @@ def test_reduce_scatter_rejects(kw, status):
     assert L.tp_last_error().decode() != ""
 
 
+def test_reduce_scatter_rejects_oversized_grid():
+    assert rs(batch=1 << 30, seq=1 << 20, N=1 << 20) == tt.TP_ERR_UNSUPPORTED
+
+
 def test_reduce_scatter_empty_batch_is_a_no_op():
     assert rs(batch=0) == tt.TP_OK
     assert rs(batch=0, parts=[None, None, None, None], z=None, ys=None, res=None) == tt.TP_OK

@@ -75,6 +75,17 @@ def test_qwi_swiglu_integer_exact(shape, tile):
     _check_exact(q, y, att, q_ref, y_ref, f"tile {tile} {shape}")
 
 
+@pytest.mark.parametrize("shape", [(37, 40, 2, 0, 3, 10, 1, 0),     # E % 32 != 0: register-staged loop; fph 5
+                                   (5, 8, 3, 1, 1, 2, 3, 2)])       # E 8, one query column, fph 1, h_r 1
+def test_qwi_swiglu_small_and_register_path(shape):
+    M, E, heads, padded, qkv, ff, tp, rank = shape
+    h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
+    x, w = _exact_inputs(M, E, h_r * qph, 13 + E)
+    q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
+    q, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank)
+    _check_exact(q, y, att, q_ref, y_ref, f"small {shape}")
+
+
 @pytest.mark.parametrize("path", [0, 1])
 def test_qwi_swiglu_both_main_loops(path):
     M, E, heads, padded, qkv, ff, tp, rank = SHAPES[0]
