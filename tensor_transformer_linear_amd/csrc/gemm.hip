@@ -20,6 +20,12 @@
 //   RMS-normalised on its way into LDS.
 // The output stage adds the bias, applies GELU, rounds once and stores bf16
 // or f32 at the (possibly remapped) output column, or adds into f32.
+//
+// A per-head row map lets a launch read a slice of every head's weight rows (the
+// query columns of a fused q_wi weight), and the SwiGLU mode pairs each output
+// column's gate and value rows in one tile: the output stage then stores
+// bf16(swish(gate) * value) at a per-head output column ([palm] the q_wi and
+// SwiGLU steps). Both are compiled only into the MAPPED instantiations.
 #include "common.h"
 #include "kernels.h"
 
