@@ -9,8 +9,10 @@
 // sub-tile of 32x32 blocks computed with v_mfma_f32_32x32x16_bf16 from 16-byte
 // LDS reads. Two main loops feed the LDS:
 // * direct-to-LDS (the default when K % 32 == 0 and A needs no transform): each
-//   32-wide K step goes global -> LDS with global_load_lds_dwordx4 into a ring of
-//   stages, several in flight. The 256x256 tile runs eight waves in two groups
+//   32-wide K step goes global -> LDS into a ring of stages, several in flight,
+//   through buffer_load_dwordx4 ... lds where a wave's blocks of a stage are
+//   contiguous (one M0 and one scalar K offset serve them all), through
+//   global_load_lds_dwordx4 otherwise. The 256x256 tile runs eight waves in two groups
 //   that ping-pong (one group multiplies while the other reads its next
 //   fragments and issues the next loads); other tiles double-buffer the operand
 //   fragments in registers so the LDS reads of one half-step overlap the MFMAs
@@ -384,6 +386,29 @@ __device__ __forceinline__ void dma_load16(const void* g, lds_byte* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
+// Buffer-resource form of the same transfer. The LDS destination is M0 plus the instruction
+// offset plus 16 * lane, and the instruction offset also moves the global source, so a wave
+// whose blocks sit next to each other in LDS sets M0 once per stage and reaches its next
+// three blocks through the offset field (at most 4095 bytes); the K advance rides in the
+// scalar offset. Raw-buffer word 3 for gfx9: 32-bit data format, no swizzle, no stride.
+constexpr int BUF_BACKOFF = 4096;  // the resource base sits this far below the tile's first row
+constexpr int BUF_MAX_BLOCKS = 4;  // 1 KB blocks one M0 covers: offsets 0, 1, 2 and 3 KB
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const unsigned char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base - BUF_BACKOFF), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+template <int IMM>
+__device__ __forceinline__ void buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, lds_byte* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds, 16, voff, soff, IMM, 0);
+}
+
+// A tile loads through buffer resources when each wave's blocks of a stage are contiguous,
+// within one operand and within one M0's reach.
+template <int BM, int BN, int NWAVE>
+constexpr bool tile_uses_buffer_loads() {
+  constexpr int nblk = (BM + BN) / 16, per_wave = (nblk + NWAVE - 1) / NWAVE;
+  return nblk == NWAVE * per_wave && (BM / 16) % per_wave == 0 && per_wave <= BUF_MAX_BLOCKS;
+}
+
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
 // SCHED selects the main-loop schedule: 0 = every wave multiplies while its own next reads fly
@@ -427,28 +452,52 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
   const int nk = K / (DROW / ESZ);    // a stage is 64 bytes of every row
 
-  // Per DMA block this wave issues: the global source of this lane's 16 bytes.
+  // Per DMA block this wave issues: the source of this lane's 16 bytes. With buffer loads a
+  // wave owns blocks [BPW w, BPW (w + 1)) and addresses them from the first row of the tile in
+  // its operand (rows past M or N clamp to the last row, never below the first); otherwise
+  // blocks w, w + NWAVE, ... from the operands' base pointers.
+  constexpr bool BUF = tile_uses_buffer_loads<BM, BN, NWAVE>();
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int blk0 = BUF ? wave_s * BLK_PER_WAVE : 0;
+  const bool wave_a = blk0 < NBLK_A;
+  const int nb_first = tile_b_row<BN, MAPPED>(p, n0, 0);
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.A) + (int64_t)m0 * p.lda * ESZ;
+  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.B) + (int64_t)nb_first * p.ldb * ESZ;
+  const __amdgpu_buffer_rsrc_t rsrc = buf_rsrc(wave_a ? abase : bbase);
   const unsigned char* src[BLK_PER_WAVE];
+  uint32_t voff[BLK_PER_WAVE];
   int dst[BLK_PER_WAVE];
 #pragma unroll
   for (int b = 0; b < BLK_PER_WAVE; ++b) {
-    const int blk = wave + b * NWAVE;
+    const int blk = BUF ? blk0 + b : wave + b * NWAVE;
     const int row = (blk < NBLK_A ? blk : blk - NBLK_A) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);  // logical chunk stored at this lane's slot
+    int64_t off;                                 // bytes from the tile's first row
     if (blk < NBLK_A) {
       const int gm = min(m0 + row, M - 1);
-      src[b] = reinterpret_cast<const unsigned char*>(p.A) + ((int64_t)gm * p.lda) * ESZ + c * 16;
+      off = ((int64_t)(gm - m0) * p.lda) * ESZ + c * 16;
+      src[b] = abase + off;
     } else {
-      const int gn = blk < NBLK ? tile_b_row<BN, MAPPED>(p, n0, row) : 0;
-      src[b] = reinterpret_cast<const unsigned char*>(p.B) + ((int64_t)gn * p.ldb) * ESZ + c * 16;
+      const int gn = blk < NBLK ? tile_b_row<BN, MAPPED>(p, n0, row) : nb_first;
+      off = ((int64_t)(gn - nb_first) * p.ldb) * ESZ + c * 16;
+      src[b] = bbase + off;
     }
+    voff[b] = (uint32_t)(off + BUF_BACKOFF - b * 1024);
     dst[b] = blk * 1024;
   }
   auto issue = [&](int kt) {
     kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
     lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
+    if constexpr (BUF) {
+      lds_byte* wbase = base + blk0 * 1024;
+      static_for<BLK_PER_WAVE>([&](auto b) {
+        constexpr int bi = decltype(b)::value;
+        buf_load16<bi * 1024>(rsrc, voff[bi], kt * DROW, wbase);
+      });
+    } else {
 #pragma unroll
-    for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + (int64_t)kt * DROW, base + dst[b]);
+      for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + (int64_t)kt * DROW, base + dst[b]);
+    }
   };
 
   f32x16_t acc[FM][FN];
@@ -596,6 +645,24 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   }
 }
 
+// Whether every buffer-loaded byte of a BM x BN tile lies within the 2^31 - 1 bytes a buffer
+// resource covers from the tile's first row: (BM - 1) rows of A; for B, BN consecutive rows or,
+// through the per-head map (non-decreasing when the head pitch is at least the head width and
+// values follow their gates), the rows of BN (SwiGLU: BN / 2) columns plus the value offset.
+bool buffer_span_ok(const GemmProblem& p, int BM, int BN) {
+  const int64_t esz = p.fp8 ? 1 : 2;
+  const int64_t tail = (int64_t)p.K * esz + BUF_BACKOFF + DROW;
+  if ((int64_t)(BM - 1) * p.lda * esz + tail > INT32_MAX) return false;
+  int64_t rows = BN;
+  if (p.ep.glu || p.b_head_w > 0) {
+    if ((p.ep.glu && p.ep.glu_off < 0) || (p.b_head_w > 0 && p.b_head_pitch < p.b_head_w)) return false;
+    const int64_t cols = p.ep.glu ? BN / 2 : BN;
+    rows = cols + (p.ep.glu ? p.ep.glu_off : 0);
+    if (p.b_head_w > 0) rows += (cols / p.b_head_w + 1) * (int64_t)(p.b_head_pitch - p.b_head_w);
+  }
+  return (rows - 1) * p.ldb * esz + tail <= INT32_MAX;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int SCHED = 0>
 hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int bn_out = p.ep.glu ? BN / 2 : BN;  // output columns per tile
@@ -603,7 +670,8 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const int nb = tiles_m * tiles_n;
   const int group_m = tiles_m < 4 ? tiles_m : 4;  // 4 M-tiles per group: measured best for L2 reuse
   dim3 grid(nb), block(WAVES_M * WAVES_N * 64);
-  const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0;
+  const bool dma_ok = p.row_r == nullptr && p.K % DBK == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
+                      (!tile_uses_buffer_loads<BM, BN, WAVES_M * WAVES_N>() || buffer_span_ok(p, BM, BN));
   if (path == GEMM_PATH_DMA && !dma_ok) return hipErrorInvalidValue;
   // the per-head row map and SwiGLU run in their own instantiations (never with RMSNorm staging)
   const bool mapped = p.ep.glu || p.b_head_w > 0;
@@ -632,6 +700,8 @@ template <int BM, int BN>
 hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int group_m = tiles_m < 4 ? tiles_m : 4;
+  static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
+  if (!buffer_span_ok(p, BM, BN)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
                      tiles_m, tiles_n, group_m);
   return hipGetLastError();
