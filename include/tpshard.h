@@ -147,7 +147,8 @@ TP_API int tp_quantize_rows_e4m3(const void* x, int64_t M, int64_t K, void* q, f
  * w_q       device uint8 [N_r, K]: E4M3 codes of the rank's weight rows, w_scale f32 [N_r]
  *           (one scale per output channel), same row map as tp_column_linear
  * K % 64 == 0. Everything else (bias, act, y, y_dtype, layout, ldy, M = 0) as
- * tp_column_linear. Errors: as tp_column_linear, TP_ERR_UNSUPPORTED for K % 64.
+ * tp_column_linear. Errors: as tp_column_linear, TP_ERR_UNSUPPORTED for K % 64 and for
+ * operands whose rows within one tile (up to 256 of them) span more than 2^31 - 1 bytes.
  */
 TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
                                 const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes,

@@ -485,9 +485,9 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
     voff[b] = (uint32_t)(off + BUF_BACKOFF - b * 1024);
     dst[b] = blk * 1024;
   }
-  auto issue = [&](int kt) {
-    kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
-    lds_byte* base = (lds_byte*)smem + (kt % STAGES) * STAGE;
+  // Stage kt (0 <= kt < nk) into ring slot `slot` (kt % STAGES).
+  auto issue_at = [&](int kt, unsigned slot) {
+    lds_byte* base = (lds_byte*)smem + slot * STAGE;
     if constexpr (BUF) {
       lds_byte* wbase = base + blk0 * 1024;
       static_for<BLK_PER_WAVE>([&](auto b) {
@@ -498,6 +498,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
 #pragma unroll
       for (int b = 0; b < BLK_PER_WAVE; ++b) dma_load16(src[b] + (int64_t)kt * DROW, base + dst[b]);
     }
+  };
+  auto issue = [&](int kt) {
+    kt = kt < nk ? kt : nk - 1;  // clamped: the loop issues unconditionally
+    issue_at(kt, (unsigned)kt % STAGES);
   };
 
   f32x16_t acc[FM][FN];
@@ -582,10 +586,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       __builtin_amdgcn_sched_barrier(0);
     }
     Frag f0, f1;
-    for (int kt = 0; kt < nk; ++kt) {
-      read(f0, kt % STAGES, 0);
-      read(f1, kt % STAGES, 1);
-      issue(kt + STAGES - 1);
+    // K step kt: read slot rs, stage k_in into slot is
+    auto step = [&](unsigned rs, int k_in, unsigned is) {
+      read(f0, rs, 0);
+      read(f1, rs, 1);
+      __builtin_amdgcn_sched_barrier(0);  // the reads first: loads issued ahead of them stall this wave
+      issue_at(k_in, is);
       wait_barrier(std::integral_constant<int, (STAGES - 2) * BLK_PER_WAVE>{}, std::integral_constant<int, 0>{});
       __builtin_amdgcn_s_setprio(1);  // the multiplying wave first: the other group only issues memory work
       if constexpr (FP8) {
@@ -598,6 +604,18 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // STAGES steps per iteration while no issued stage needs clamping: every ring slot is a
+    // constant, so the LDS addresses are immediates and M0 a constant
+    int kt = 0;
+    for (; kt + 2 * STAGES - 1 <= nk; kt += STAGES)
+      static_for<STAGES>([&](auto u) {
+        constexpr unsigned U = decltype(u)::value;
+        step(U, kt + U + STAGES - 1, (U + STAGES - 1) % STAGES);
+      });
+    for (; kt < nk; ++kt) {
+      const int k_in = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;  // clamped past the last stage
+      step((unsigned)kt % STAGES, k_in, (unsigned)k_in % STAGES);
     }
     if (wm == 0) {
       __builtin_amdgcn_s_barrier();
@@ -646,17 +664,18 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
 }
 
 // Whether every buffer-loaded byte of a BM x BN tile lies within the 2^31 - 1 bytes a buffer
-// resource covers from the tile's first row: (BM - 1) rows of A; for B, BN consecutive rows or,
-// through the per-head map (non-decreasing when the head pitch is at least the head width and
-// values follow their gates), the rows of BN (SwiGLU: BN / 2) columns plus the value offset.
+// resource covers from the tile's first row: min(BM, M) rows of A; for B, min(BN, N) consecutive
+// rows or, through the per-head map (non-decreasing when the head pitch is at least the head
+// width and values follow their gates), the rows of BN (SwiGLU: BN / 2) columns plus the value
+// offset. Rows past M or N clamp to the last one.
 bool buffer_span_ok(const GemmProblem& p, int BM, int BN) {
   const int64_t esz = p.fp8 ? 1 : 2;
   const int64_t tail = (int64_t)p.K * esz + BUF_BACKOFF + DROW;
-  if ((int64_t)(BM - 1) * p.lda * esz + tail > INT32_MAX) return false;
-  int64_t rows = BN;
+  if ((int64_t)(std::min(BM, p.M) - 1) * p.lda * esz + tail > INT32_MAX) return false;
+  int64_t rows = std::min(BN, p.N);
   if (p.ep.glu || p.b_head_w > 0) {
     if ((p.ep.glu && p.ep.glu_off < 0) || (p.b_head_w > 0 && p.b_head_pitch < p.b_head_w)) return false;
-    const int64_t cols = p.ep.glu ? BN / 2 : BN;
+    const int64_t cols = std::min(p.ep.glu ? BN / 2 : BN, p.N);
     rows = cols + (p.ep.glu ? p.ep.glu_off : 0);
     if (p.b_head_w > 0) rows += (cols / p.b_head_w + 1) * (int64_t)(p.b_head_pitch - p.b_head_w);
   }
@@ -701,7 +720,7 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
   const int group_m = tiles_m < 4 ? tiles_m : 4;
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
-  if (!buffer_span_ok(p, BM, BN)) return hipErrorInvalidValue;
+  if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
                      tiles_m, tiles_n, group_m);
   return hipGetLastError();

@@ -223,7 +223,10 @@ TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M
   p.ep.col_scale = w_scale;
   const int tile = g_tile_override == tpk::TILE_256x256 || g_tile_override == tpk::TILE_128x128 ? g_tile_override
                                                                                                    : tpk::TILE_AUTO;
-  return hip_status(tpk::launch_gemm_fp8(p, tile, as_stream(stream)), "tp_column_linear_fp8 launch");
+  const hipError_t e = tpk::launch_gemm_fp8(p, tile, as_stream(stream));
+  if (e == hipErrorNotSupported)
+    return fail(TP_ERR_UNSUPPORTED, "a tile's operand rows span more than 2^31 - 1 bytes (K = %lld)", (long long)K);
+  return hip_status(e, "tp_column_linear_fp8 launch");
 }
 
 TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,

@@ -180,3 +180,35 @@ def test_empty_input():
     w = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
     tt.tp_column_linear(x, w, None, [64], 1, 0, y=y)
     torch.cuda.synchronize()
+
+
+def test_buffer_load_span_limit():
+    """The direct-to-LDS loads of the eight-wave 256x256 tile go through buffer resources that
+    reach 2^31 - 1 bytes from a tile's first row. At K = 4194272 a full tile's last A and B rows
+    sit just inside that reach, so the forced direct-to-LDS path runs with its largest offsets;
+    at K = 4194304 they do not: the forced path is refused and the automatic one falls back to
+    register staging. Values in {-1, 0, 1} keep every float32 partial sum exact (|sum| < 2^24),
+    so sampled outputs match the oracle bit for bit."""
+    M = N = 256
+    rows, cols = [0, 1, 130, 255], [0, 77, 128, 255]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(991)
+    for K, fits in ((4194272, True), (4194304, False)):
+        x = torch.randint(-1, 2, (M, K), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+        w = torch.randint(-1, 2, (N, K), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+        tt.set_gemm_tile(0)
+        tt.set_gemm_path(tt.GEMM_PATH_DMA)
+        if fits:
+            y = tt.tp_column_linear(x, w, None, [N], 1, 0)
+        else:
+            with pytest.raises(RuntimeError):
+                tt.tp_column_linear(x, w, None, [N], 1, 0)
+            tt.set_gemm_path(tt.GEMM_PATH_AUTO)
+            y = tt.tp_column_linear(x, w, None, [N], 1, 0)
+        torch.cuda.synchronize()
+        xs = host_bits(x[rows].contiguous())
+        ws = host_bits(w[cols].contiguous())
+        got = host_bits(y)[np.ix_(rows, cols)]
+        assert np.array_equal(got, oracle.column_linear(xs, ws, None, [len(cols)], 1, 0)), f"K = {K}"
+        del x, w, y
+        torch.cuda.empty_cache()
