@@ -401,12 +401,23 @@ __device__ __forceinline__ void buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds, 16, voff, soff, IMM, 0);
 }
 
-// A tile loads through buffer resources when each wave's blocks of a stage are contiguous,
-// within one operand and within one M0's reach.
+// How a tile's waves split the 1 KB blocks of a stage for buffer loads, each run of a wave's
+// blocks contiguous in LDS, within one operand and within one M0's reach:
+// 1 = wave w owns blocks [P w, P (w + 1)), all of one operand (P blocks per wave);
+// 2 = wave w owns A blocks [PA w, PA (w + 1)) and B blocks NBLK_A + [PB w, PB (w + 1)) (B
+//     blocks past the tile's rows are padding that reads a valid row);
+// 0 = neither fits: per-lane global_load_lds.
+template <int BM, int BN, int NWAVE>
+constexpr int tile_buffer_mode() {
+  constexpr int na = BM / 16, nb = BN / 16, per_wave = (na + nb + NWAVE - 1) / NWAVE;
+  if (na + nb == NWAVE * per_wave && na % per_wave == 0 && per_wave <= BUF_MAX_BLOCKS) return 1;
+  constexpr int pa = na / NWAVE, pb = (nb + NWAVE - 1) / NWAVE;
+  if (na % NWAVE == 0 && pa + pb == per_wave && pa <= BUF_MAX_BLOCKS && pb <= BUF_MAX_BLOCKS) return 2;
+  return 0;
+}
 template <int BM, int BN, int NWAVE>
 constexpr bool tile_uses_buffer_loads() {
-  constexpr int nblk = (BM + BN) / 16, per_wave = (nblk + NWAVE - 1) / NWAVE;
-  return nblk == NWAVE * per_wave && (BM / 16) % per_wave == 0 && per_wave <= BUF_MAX_BLOCKS;
+  return tile_buffer_mode<BM, BN, NWAVE>() != 0;
 }
 
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
@@ -452,24 +463,27 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
   const int nk = K / (DROW / ESZ);    // a stage is 64 bytes of every row
 
-  // Per DMA block this wave issues: the source of this lane's 16 bytes. With buffer loads a
-  // wave owns blocks [BPW w, BPW (w + 1)) and addresses them from the first row of the tile in
-  // its operand (rows past M or N clamp to the last row, never below the first); otherwise
-  // blocks w, w + NWAVE, ... from the operands' base pointers.
-  constexpr bool BUF = tile_uses_buffer_loads<BM, BN, NWAVE>();
+  // Per DMA block this wave issues: the source of this lane's 16 bytes, addressed from the
+  // tile's first row of its operand (rows past M or N clamp to the last row, never below the
+  // first). Buffer-load modes 1 and 2 give each wave contiguous runs of blocks (one run per
+  // operand it loads, one M0 and one resource each); otherwise blocks w, w + NWAVE, ...
+  constexpr int MODE = tile_buffer_mode<BM, BN, NWAVE>();
+  constexpr int PA = MODE == 1 ? BLK_PER_WAVE : MODE == 2 ? NBLK_A / NWAVE : 0;  // blocks of the first run
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int blk0 = BUF ? wave_s * BLK_PER_WAVE : 0;
-  const bool wave_a = blk0 < NBLK_A;
+  // first block of each run: mode 1, one run (A or B by wave); mode 2, the A run then the B run
+  const int run0 = MODE == 2 ? wave_s * PA : wave_s * BLK_PER_WAVE;
+  const int run1 = MODE == 2 ? NBLK_A + wave_s * (BLK_PER_WAVE - PA) : run0;
   const int nb_first = tile_b_row<BN, MAPPED>(p, n0, 0);
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.A) + (int64_t)m0 * p.lda * ESZ;
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.B) + (int64_t)nb_first * p.ldb * ESZ;
-  const __amdgpu_buffer_rsrc_t rsrc = buf_rsrc(wave_a ? abase : bbase);
+  const __amdgpu_buffer_rsrc_t rsrc0 = buf_rsrc(MODE == 2 || run0 < NBLK_A ? abase : bbase);
+  const __amdgpu_buffer_rsrc_t rsrc1 = buf_rsrc(bbase);
   const unsigned char* src[BLK_PER_WAVE];
   uint32_t voff[BLK_PER_WAVE];
   int dst[BLK_PER_WAVE];
 #pragma unroll
   for (int b = 0; b < BLK_PER_WAVE; ++b) {
-    const int blk = BUF ? blk0 + b : wave + b * NWAVE;
+    const int blk = MODE == 0 ? wave + b * NWAVE : b < PA ? run0 + b : run1 + (b - PA);
     const int row = (blk < NBLK_A ? blk : blk - NBLK_A) * 16 + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);  // logical chunk stored at this lane's slot
     int64_t off;                                 // bytes from the tile's first row
@@ -482,17 +496,19 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
       off = ((int64_t)(gn - nb_first) * p.ldb) * ESZ + c * 16;
       src[b] = bbase + off;
     }
-    voff[b] = (uint32_t)(off + BUF_BACKOFF - b * 1024);
+    voff[b] = (uint32_t)(off + BUF_BACKOFF - (b < PA ? b : b - PA) * 1024);
     dst[b] = blk * 1024;
   }
   // Stage kt (0 <= kt < nk) into ring slot `slot` (kt % STAGES).
   auto issue_at = [&](int kt, unsigned slot) {
     lds_byte* base = (lds_byte*)smem + slot * STAGE;
-    if constexpr (BUF) {
-      lds_byte* wbase = base + blk0 * 1024;
+    if constexpr (MODE != 0) {
       static_for<BLK_PER_WAVE>([&](auto b) {
         constexpr int bi = decltype(b)::value;
-        buf_load16<bi * 1024>(rsrc, voff[bi], kt * DROW, wbase);
+        if constexpr (bi < PA)
+          buf_load16<bi * 1024>(rsrc0, voff[bi], kt * DROW, base + run0 * 1024);
+        else
+          buf_load16<(bi - PA) * 1024>(rsrc1, voff[bi], kt * DROW, base + run1 * 1024);
       });
     } else {
 #pragma unroll
@@ -645,18 +661,31 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   Frag f0, f1;
   read(f0, 0, 0);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // both edges into the loop arrive with no reads pending
-  for (int kt = 0; kt < nk; ++kt) {
-    read(f1, kt % STAGES, 1);
+  // K step kt: slot rs holds stage kt, stage k_in goes into slot is, slot rn holds stage kt + 1
+  // (past the last step: a slot of clamped data, never multiplied)
+  auto step = [&](unsigned rs, int k_in, unsigned is, unsigned rn) {
+    read(f1, rs, 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(f0);
     wait_barrier(std::integral_constant<int, (STAGES - 3) * BLK_PER_WAVE>{}, std::integral_constant<int, 0>{});
-    issue(kt + STAGES - 1);
-    read(f0, (kt + 1) % STAGES, 0);  // past the last step: a slot of clamped data, never multiplied
+    issue_at(k_in, is);
+    read(f0, rn, 0);
     __builtin_amdgcn_sched_barrier(0);
     mma(f1);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // STAGES steps per iteration while no issued stage needs clamping (constant ring slots)
+  int kt = 0;
+  for (; kt + 2 * STAGES - 1 <= nk; kt += STAGES)
+    static_for<STAGES>([&](auto u) {
+      constexpr unsigned U = decltype(u)::value;
+      step(U, kt + U + STAGES - 1, (U + STAGES - 1) % STAGES, (U + 1) % STAGES);
+    });
+  for (; kt < nk; ++kt) {
+    const int k_in = kt + STAGES - 1 < nk ? kt + STAGES - 1 : nk - 1;
+    step((unsigned)kt % STAGES, k_in, (unsigned)k_in % STAGES, (unsigned)(kt + 1) % STAGES);
   }
   __syncthreads();
   gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
