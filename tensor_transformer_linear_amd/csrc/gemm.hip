@@ -692,6 +692,201 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   }
 }
 
+// Ping-pong 256x256 tile on paired K steps. An LDS row holds two consecutive K steps (128
+// bytes: 64 bf16 or 128 E4M3 values), so the eight lanes that fetch a row of a 1 KB block (8
+// rows) read one whole 128-byte line: half the cache requests of 64-byte rows for the same
+// bytes. The 16-byte chunk index is XORed with bits 1..3 of the row, so the 16 consecutive rows
+// one ds_read_b128 phase reads fall on 16 distinct bank groups (row parity picks the half of
+// the 256-byte bank window).
+//
+// The ring is five 32 KB slots (160 KB). Half h is the A rows (h even) or the B rows (h odd)
+// of K pair h / 2 and lives in slot h % 5. Memory phase k (the two groups run the same
+// ping-pong as the 64-byte-row kernel) reads step k from halves 2 (k / 2) and 2 (k / 2) + 1,
+// issues half k + 3 into the slot of half k - 2 (which both groups finished reading at step
+// k - 1 at the latest, one barrier earlier), and waits until step k + 1's halves have landed:
+// the halves issued after them are k + 2 and k + 3 for even k, k + 3 for odd k (8 or 4 of
+// this wave's loads may stay outstanding). Halves past the last pair reload the last pair
+// into its own slot (identical bytes), so every phase issues the same loads. Each wave owns a
+// run of four A blocks and four B blocks (one M0 and one buffer resource each).
+__device__ __forceinline__ int pair_off(int row, int lc) { return row * 128 + ((lc ^ ((row >> 1) & 7)) << 4); }
+
+template <bool FP8, bool MAPPED>
+__global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int tiles_m, int tiles_n, int group_m) {
+  constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, WM = 128, WN = 64, FM = 4, FN = 2;
+  constexpr int HALF = 256 * 128, SLOTS = 5, RUN = 4;  // a wave's blocks per half
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SLOTS * HALF];
+  static_assert(SLOTS * HALF >= WAVES_M * 32 * (BN + 4) * 4, "the output stage reuses the ring");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = group_m * tiles_n;
+  const int grp = lid / per_group, first_m = grp * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
+  const int in = lid - grp * per_group;
+  const int m0 = (first_m + in % gsz) * BM, n0 = (in / gsz) * (MAPPED && p.ep.glu ? BN / 2 : BN);
+  const int M = p.M, K = p.K;
+  constexpr int ESZ = FP8 ? 1 : 2;
+  const int nk = K / (64 / ESZ);  // 64-byte K steps; K fills whole pairs
+  const int np = nk / 2;
+
+  // This wave's blocks: rows 8 (RUN w + b) + lane / 8 of each operand's tile, physical chunk
+  // lane % 8 of the 128-byte LDS row, fetched from logical chunk (lane % 8) ^ ((row / 2) % 8).
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int nb_first = tile_b_row<BN, MAPPED>(p, n0, 0);
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.A) + (int64_t)m0 * p.lda * ESZ;
+  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.B) + (int64_t)nb_first * p.ldb * ESZ;
+  const __amdgpu_buffer_rsrc_t rsrc_a = buf_rsrc(abase), rsrc_b = buf_rsrc(bbase);
+  uint32_t voff_a[RUN], voff_b[RUN];
+#pragma unroll
+  for (int b = 0; b < RUN; ++b) {
+    const int row = (RUN * wave_s + b) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
+    const int gm = min(m0 + row, M - 1);
+    const int gn = tile_b_row<BN, MAPPED>(p, n0, row);
+    voff_a[b] = (uint32_t)(((int64_t)(gm - m0) * p.lda) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
+    voff_b[b] = (uint32_t)(((int64_t)(gn - nb_first) * p.ldb) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
+  }
+  // Half h (pair h / 2, clamped to the last pair) into slot `slot` (h % 5, or the clamped
+  // half's slot): A rows for even h, B rows for odd h.
+  auto issue_half = [&](int pair, bool b_rows, unsigned slot) {
+    lds_byte* base = (lds_byte*)smem + slot * HALF + wave_s * RUN * 1024;
+    static_for<RUN>([&](auto b) {
+      constexpr int bi = decltype(b)::value;
+      if (b_rows)
+        buf_load16<bi * 1024>(rsrc_b, voff_b[bi], pair * 128, base);
+      else
+        buf_load16<bi * 1024>(rsrc_a, voff_a[bi], pair * 128, base);
+    });
+  };
+  auto issue_clamped = [&](int h) {
+    const int hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
+    issue_half(hc >> 1, hc & 1, (unsigned)hc % SLOTS);
+  };
+
+  f32x16_t acc[FM][FN];
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) { static_for<16>([&](auto v) { acc[i][j][decltype(v)::value] = 0.0f; }); });
+  });
+  const int a_row0 = wm * WM + (lane & 31), b_row0 = wn * WN + (lane & 31);
+  const int khalf = lane >> 5;
+  struct Frag {
+    bf16x8_t a[FM], b[FN];
+  };
+  // Fragment `half` of step k from slots sa (A) and sb (B): the 64-byte half kp = k % 2 of the
+  // rows, then as in the 64-byte-row kernel (bf16: chunk 2 half + l / 32; fp8: 2 (l / 32) + half).
+  // Rows 32 apart share the swizzle, so one per-lane offset per (kp, half) serves every block.
+  int off_a[2][2], off_b[2][2];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int lc = kp * 4 + (FP8 ? khalf * 2 + hf : hf * 2 + khalf);
+      off_a[kp][hf] = pair_off(a_row0, lc);
+      off_b[kp][hf] = pair_off(b_row0, lc);
+    }
+  auto read = [&](Frag& f, unsigned sa, unsigned sb, int kp, int half) {
+    const unsigned char* pa = smem + (sa * HALF + off_a[kp][half]);
+    const unsigned char* pb = smem + (sb * HALF + off_b[kp][half]);
+    static_for<FM>([&](auto i) {
+      f.a[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pa + i * 32 * 128));
+    });
+    static_for<FN>([&](auto j) {
+      f.b[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(pb + j * 32 * 128));
+    });
+  };
+  auto mma8 = [&](const Frag& f0, const Frag& f1) {
+    static_for<FM>([&](auto i) {
+      static_for<FN>([&](auto j) {
+        const i32x8_t a = __builtin_bit_cast(
+            i32x8_t, __builtin_shufflevector(__builtin_bit_cast(u32x4_t, f0.a[i]), __builtin_bit_cast(u32x4_t, f1.a[i]),
+                                             0, 1, 2, 3, 4, 5, 6, 7));
+        const i32x8_t b = __builtin_bit_cast(
+            i32x8_t, __builtin_shufflevector(__builtin_bit_cast(u32x4_t, f0.b[j]), __builtin_bit_cast(u32x4_t, f1.b[j]),
+                                             0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 0, 0, 0);
+      });
+    });
+  };
+  auto mma = [&](const Frag& f) {
+    static_for<FM>([&](auto i) {
+      static_for<FN>([&](auto j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      });
+    });
+  };
+  // s_waitcnt vmcnt(VM) lgkmcnt(LGKM) (expcnt open) and a fence-free workgroup barrier
+  auto wait_barrier = [&](auto vm, auto lgkm) {
+    constexpr int VM = decltype(vm)::value, LGKM = decltype(lgkm)::value;
+    static_assert(VM >= 0 && VM < 64, "vmcnt immediate is six bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (LGKM << 8) | ((VM >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: halves 0, 1, 2; pair 0 (halves 0 and 1) landed everywhere. Group 1 runs one
+  // phase behind group 0 (an extra barrier at its start, one at group 0's end).
+  issue_clamped(0);
+  issue_clamped(1);
+  issue_clamped(2);
+  wait_barrier(std::integral_constant<int, RUN>{}, std::integral_constant<int, 15>{});
+  if (wm == 1) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  Frag f0, f1;
+  // memory phase of step k (reads from slots sa, sb at pair half kp; issues `pair`'s A or B
+  // rows into slot is), then the compute phase
+  auto step = [&](unsigned sa, unsigned sb, int kp, int pair, bool b_rows, unsigned is, auto vm) {
+    read(f0, sa, sb, kp, 0);
+    read(f1, sa, sb, kp, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_half(pair, b_rows, is);
+    wait_barrier(vm, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (FP8) {
+      mma8(f0, f1);
+    } else {
+      mma(f0);
+      mma(f1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Two steps (one K pair) per iteration: the pair half kp and the waits are constants; slots
+  // are scalars kept by increments, so each fragment read adds one slot offset to a per-lane
+  // base. Pair j reads slots sa = 2j % 5 and sa + 1 and issues halves 2j + 3 and 2j + 4 into
+  // slots (sa + 3) % 5 and (sa + 4) % 5; the last two pairs clamp their issues.
+  unsigned sa = 0;
+  auto next = [](unsigned v, unsigned d) { return v + d >= SLOTS ? v + d - SLOTS : v + d; };
+  int j = 0;
+  for (; j < np - 2; ++j) {
+    const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
+    step(sa, sb, 0, j + 1, true, next(sa, 3), std::integral_constant<int, 2 * RUN>{});
+    step(sa, sb, 1, j + 2, false, next(sa, 4), std::integral_constant<int, RUN>{});
+    sa = next(sa, 2);
+  }
+  for (; j < np; ++j) {
+    const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
+    int h = 2 * j + 3, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
+    step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, 2 * RUN>{});
+    h = 2 * j + 4, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
+    step(sa, sb, 1, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, RUN>{});
+    sa = next(sa, 2);
+  }
+  if (wm == 0) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
 // Whether every buffer-loaded byte of a BM x BN tile lies within the 2^31 - 1 bytes a buffer
 // resource covers from the tile's first row: min(BM, M) rows of A; for B, min(BN, N) consecutive
 // rows or, through the per-head map (non-decreasing when the head pitch is at least the head
@@ -725,6 +920,16 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const bool mapped = p.ep.glu || p.b_head_w > 0;
   if (mapped && p.row_r != nullptr) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER) {
+    if constexpr (BM == 256 && BN == 256 && WAVES_M == 2 && WAVES_N == 4 && SCHED == 1) {
+      if (p.K % 64 == 0) {  // whole K pairs: 128-byte LDS rows
+        if (mapped)
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<false, true>), grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+        else
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<false, false>), grid, block, 0, stream, p, tiles_m, tiles_n,
+                             group_m);
+        return hipGetLastError();
+      }
+    }
     if (mapped)
       hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, SCHED, false, true>), grid, block, 0,
                          stream, p, tiles_m, tiles_n, group_m);
@@ -750,6 +955,13 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   const int group_m = tiles_m < 4 ? tiles_m : 4;
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
   if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
+  if constexpr (BM == 256 && BN == 256) {
+    if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
+      hipLaunchKernelGGL((gemm_nt_pair_kernel<true, false>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
+                         tiles_m, tiles_n, group_m);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
                      tiles_m, tiles_n, group_m);
   return hipGetLastError();

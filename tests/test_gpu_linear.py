@@ -212,3 +212,21 @@ def test_buffer_load_span_limit():
         assert np.array_equal(got, oracle.column_linear(xs, ws, None, [len(cols)], 1, 0)), f"K = {K}"
         del x, w, y
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K", [64, 128, 448, 1344])
+def test_paired_k_rows_tile_integer_exact(K):
+    """The 256x256 tile on whole 64-wide K pairs stages two K steps per 128-byte LDS row: one
+    pair (the prologue's third half reloads the last pair), a few pairs (every issue past the
+    end reloads it), and 21 pairs (the five-slot ring wraps several times). Ragged M and N,
+    a sub-parameter boundary inside the tile, bias, GELU; bit-exact on integer inputs."""
+    tt.set_gemm_tile(0)
+    tt.set_gemm_path(tt.GEMM_PATH_DMA)
+    M, sizes, tp, rank = 301, [300, 76, 76], 2, 1
+    x, w, b, w_r, b_r = _int_inputs(M, K, sizes, tp, rank, 40 + K)
+    y = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, y_dtype=tt.TP_DTYPE_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f32(y), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, out_dtype=oracle.OUT_F32))
+    yg = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, act=tt.TP_ACT_GELU_ERF)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(yg), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=tt.TP_ACT_GELU_ERF))
