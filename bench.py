@@ -232,8 +232,8 @@ def cpu_baseline(budget_s: float):
 # step's time; its normalisation pass is a separate kernel). Its launches are timed alone after
 # the timed steps, with HIP events on the stream it runs on, on the normalised rows the fused
 # entry point materialises: the same kernel, shape and tile as inside the step.
-DOMINANT = {4: ("column GEMM [32768 x 8192] x [3072 x 8192]^T -> bf16", "gemm_nt_dma_kernel"),
-            3: ("c_proj row partial [8192 x 1792] x [4096 x 1792]^T -> f32", "gemm_nt_dma_kernel"),
+DOMINANT = {4: ("column GEMM [32768 x 8192] x [3072 x 8192]^T -> bf16", "gemm_nt_pair_kernel"),
+            3: ("c_proj row partial [8192 x 1792] x [4096 x 1792]^T -> f32", "gemm_nt_pair_kernel"),
             2: ("fused-QKV column GEMM [4096 x 4096] x [768 x 4096]^T + bias -> bf16", "gemm_nt_dma_kernel")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_column_32768x3072x8192_hbm_traffic.txt")
 KERNEL_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm.hip", "tensor_transformer_linear_amd/csrc/common.h",
