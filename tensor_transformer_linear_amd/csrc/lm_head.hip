@@ -7,8 +7,8 @@
 // shard from HBM: every weight byte is read once.
 //
 // Two streaming kernels compute the logits; both give a workgroup a tile of weight
-// rows inside one chunk and finish with that workgroup's (max, lowest index)
-// candidate per batch row, which a second kernel launched right after reduces
+// rows and finish with that workgroup's (max, lowest index) candidate per batch
+// row, which a second kernel launched right after reduces
 // (a kernel boundary instead of per-workgroup device-scope fences, which on gfx950
 // write back and invalidate the whole L2).
 //
@@ -20,6 +20,11 @@
 //   K; weight, x and block-scale pieces go global -> LDS with global_load_lds into
 //   a ring of stages that fills the CU's LDS, so the prefetch depth costs no
 //   registers. Needs K % 32 (64-byte stages) or K % 64 (128-byte stages) for bf16.
+//   Its tiles are whole 64-row blocks of the shard: the chunks only group the
+//   concatenated output, which is the same rows in the same order, so a chunk
+//   boundary inside a block changes nothing.
+//
+// The register-streaming shapes tile each chunk on its own.
 //
 // Both multiply with v_mfma_f32_16x16x32_bf16, x as the row operand and the
 // weight as the column operand, so every lane's accumulators belong to one weight
@@ -342,20 +347,27 @@ struct LmdStage {
 };
 
 template <bool FP8, int RB, int STAGES>
-__global__ __launch_bounds__(LMD_THREADS) void lm_head_dma_kernel(LmHeadProblem p, int tiles_per_chunk, int n_tiles,
-                                                                  int b0) {
+__global__ __launch_bounds__(LMD_THREADS) void lm_head_dma_kernel(LmHeadProblem p, int n_tiles, int b0) {
   using SG = LmdStage<FP8, RB>;
   constexpr int KW = SG::KW, XB = SG::XB, STAGE = SG::BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.K, V = p.V, C = p.chunk;
+  const int K = p.K, V = p.V;
   const int nbatch = min(LM_BATCH, p.B - b0);
   const int tile = blockIdx.x;
-  const int chunk = tile / tiles_per_chunk, tin = tile - chunk * tiles_per_chunk;
-  const int row0 = chunk * C + tin * LMD_ROWS;
-  const int nrows = max(0, min(LMD_ROWS, min(V, (chunk + 1) * C) - row0));
+  const int row0 = tile * LMD_ROWS;
+  const int nrows = max(0, min(LMD_ROWS, V - row0));
   const int nst = K / KW;
   const int nblk = K / 128;
+  // Each tile walks K from its own starting stage (tile mod the stage count; E4M3 at
+  // 64-byte stages: an even stage, so that 128-wide blocks stay whole) and wraps. Tiles in
+  // flight together then read different offsets of their rows instead of the same one,
+  // which spreads the requests over the memory channels: with every tile at the same
+  // offset, the time depended on where the weight copy sat in memory (29 to 41 us for the
+  // same bytes). A row's order depends only on its 64-row block, so the logits do not
+  // depend on the chunking.
+  const int rot = (FP8 && KW < 128) ? (tile % (nst / 2)) * 2 : tile % nst;
+  auto kstage = [&](int st) { return st + rot < nst ? st + rot : st + rot - nst; };
 
   // This lane's DMA sources: weight block wave + 4 b (b < WPW) and x block wave + 4 b (b < XPW;
   // x blocks past NXB repeat x block 0 into padding). Rows past the tile or the batch read a
@@ -389,13 +401,14 @@ __global__ __launch_bounds__(LMD_THREADS) void lm_head_dma_kernel(LmHeadProblem 
   auto issue = [&](int st) {
     st = st < nst ? st : nst - 1;  // clamped: the loop issues unconditionally
     lmd_lds* base = (lmd_lds*)ring + (st % STAGES) * STAGE;
+    const int ks = kstage(st);      // the K stage this ring slot receives
 #pragma unroll
     for (int b = 0; b < SG::WPW; ++b)
-      lmd_dma16<LMD_POLICY_DEFAULT>(wsrc[b] + (size_t)st * RB, base + (wave + 4 * b) * 1024);
+      lmd_dma16<LMD_POLICY_DEFAULT>(wsrc[b] + (size_t)ks * RB, base + (wave + 4 * b) * 1024);
 #pragma unroll
     for (int b = 0; b < SG::XPW; ++b)
-      lmd_dma16<LMD_POLICY_DEFAULT>(xsrc[b] + (size_t)st * XB, base + SG::X_OFF + (wave + 4 * b) * 1024);
-    if constexpr (FP8) lmd_dma4(ssrc + st * KW / 128, base + SG::S_OFF + wave * 256);
+      lmd_dma16<LMD_POLICY_DEFAULT>(xsrc[b] + (size_t)ks * XB, base + SG::X_OFF + (wave + 4 * b) * 1024);
+    if constexpr (FP8) lmd_dma4(ssrc + ks * KW / 128, base + SG::S_OFF + wave * 256);
   };
 
   const int r16 = lane & 15, kq = lane >> 4;
@@ -641,10 +654,9 @@ void launch_shape(const LmHeadProblem& p, int b0, hipStream_t stream) {
 template <bool FP8, int RB, int STAGES>
 void launch_dma(const LmHeadProblem& p, int b0, hipStream_t stream) {
   static_assert(STAGES * LmdStage<FP8, RB>::BYTES <= 160 * 1024, "ring exceeds LDS");
-  int per;
-  const int n_tiles = lm_tiles(p.V, p.chunk, LMD_ROWS, &per);
-  hipLaunchKernelGGL((lm_head_dma_kernel<FP8, RB, STAGES>), dim3(n_tiles), dim3(LMD_THREADS), 0, stream, p, per,
-                     n_tiles, b0);
+  const int n_tiles = (p.V + LMD_ROWS - 1) / LMD_ROWS;  // whole 64-row blocks of the shard
+  hipLaunchKernelGGL((lm_head_dma_kernel<FP8, RB, STAGES>), dim3(n_tiles), dim3(LMD_THREADS), 0, stream, p, n_tiles,
+                     b0);
   hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(min(LM_BATCH, p.B - b0)), dim3(LM_FIN_THREADS), 0, stream, p, n_tiles,
                      b0);
 }
