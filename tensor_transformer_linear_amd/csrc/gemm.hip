@@ -692,28 +692,30 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   }
 }
 
-// Ping-pong 256x256 tile on paired K steps. An LDS row holds two consecutive K steps (128
+// Ping-pong square tile (256 or 128) on paired K steps. An LDS row holds two consecutive K steps (128
 // bytes: 64 bf16 or 128 E4M3 values), so the eight lanes that fetch a row of a 1 KB block (8
 // rows) read one whole 128-byte line: half the cache requests of 64-byte rows for the same
 // bytes. The 16-byte chunk index is XORed with bits 1..3 of the row, so the 16 consecutive rows
 // one ds_read_b128 phase reads fall on 16 distinct bank groups (row parity picks the half of
 // the 256-byte bank window).
 //
-// The ring is five 32 KB slots (160 KB). Half h is the A rows (h even) or the B rows (h odd)
-// of K pair h / 2 and lives in slot h % 5. Memory phase k (the two groups run the same
-// ping-pong as the 64-byte-row kernel) reads step k from halves 2 (k / 2) and 2 (k / 2) + 1,
-// issues half k + 3 into the slot of half k - 2 (which both groups finished reading at step
-// k - 1 at the latest, one barrier earlier), and waits until step k + 1's halves have landed:
-// the halves issued after them are k + 2 and k + 3 for even k, k + 3 for odd k (8 or 4 of
-// this wave's loads may stay outstanding). Halves past the last pair reload the last pair
-// into its own slot (identical bytes), so every phase issues the same loads. Each wave owns a
-// run of four A blocks and four B blocks (one M0 and one buffer resource each).
+// The ring is S slots of one operand's rows of one pair (a "half": 32 KB for 256 rows, 16 KB
+// for 128; S = 5 and 10, 160 KB). Half h is the A rows (h even) or the B rows (h odd) of K pair
+// h / 2 and lives in slot h % S. Memory phase k (the two groups run the same ping-pong as the
+// 64-byte-row kernel) reads step k from halves 2 (k / 2) and 2 (k / 2) + 1, issues half
+// k + S - 2 into the slot of half k - 2 (which both groups finished reading at step k - 1 at
+// the latest, one barrier earlier), and waits until step k + 1's halves have landed: the
+// halves issued after them are k + 2 .. k + S - 2 for even k and k + 3 .. k + S - 2 for odd
+// k. Halves past the last pair reload the last pair into its own slot (identical bytes), so
+// every phase issues the same loads. Each wave owns a run of BT / 64 A blocks and one of BT /
+// 64 B blocks (one M0 and one buffer resource each).
 __device__ __forceinline__ int pair_off(int row, int lc) { return row * 128 + ((lc ^ ((row >> 1) & 7)) << 4); }
 
-template <bool FP8, bool MAPPED>
+template <int BT, int SLOTS, bool FP8, bool MAPPED>
 __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int tiles_m, int tiles_n, int group_m) {
-  constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 4, WM = 128, WN = 64, FM = 4, FN = 2;
-  constexpr int HALF = 256 * 128, SLOTS = 5, RUN = 4;  // a wave's blocks per half
+  constexpr int BM = BT, BN = BT, WAVES_M = 2, WAVES_N = 4, WM = BT / 2, WN = BT / 4, FM = WM / 32, FN = WN / 32;
+  constexpr int HALF = BT * 128, RUN = BT / 64;  // a wave's blocks per half
+  static_assert((BT == 256 || BT == 128) && SLOTS >= 4 && (SLOTS - 3) * RUN < 64, "pair ring shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SLOTS * HALF];
   static_assert(SLOTS * HALF >= WAVES_M * 32 * (BN + 4) * 4, "the output stage reuses the ring");
 
@@ -827,12 +829,11 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: halves 0, 1, 2; pair 0 (halves 0 and 1) landed everywhere. Group 1 runs one
+  // prologue: halves 0 .. S - 3; pair 0 (halves 0 and 1) landed everywhere. Group 1 runs one
   // phase behind group 0 (an extra barrier at its start, one at group 0's end).
-  issue_clamped(0);
-  issue_clamped(1);
-  issue_clamped(2);
-  wait_barrier(std::integral_constant<int, RUN>{}, std::integral_constant<int, 15>{});
+#pragma unroll
+  for (int h = 0; h < SLOTS - 2; ++h) issue_clamped(h);
+  wait_barrier(std::integral_constant<int, (SLOTS - 4) * RUN>{}, std::integral_constant<int, 15>{});
   if (wm == 1) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -860,23 +861,25 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   };
   // Two steps (one K pair) per iteration: the pair half kp and the waits are constants; slots
   // are scalars kept by increments, so each fragment read adds one slot offset to a per-lane
-  // base. Pair j reads slots sa = 2j % 5 and sa + 1 and issues halves 2j + 3 and 2j + 4 into
-  // slots (sa + 3) % 5 and (sa + 4) % 5; the last two pairs clamp their issues.
+  // base. Pair j reads slots sa = 2j % S and sa + 1 and issues halves 2j + S - 2 and
+  // 2j + S - 1 into slots (sa + S - 2) % S and (sa + S - 1) % S; the last pairs clamp.
   unsigned sa = 0;
   auto next = [](unsigned v, unsigned d) { return v + d >= SLOTS ? v + d - SLOTS : v + d; };
+  constexpr int H0 = SLOTS - 2;  // half issued at the first step of pair 0
   int j = 0;
-  for (; j < np - 2; ++j) {
+  for (; 2 * j + SLOTS <= 2 * np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
-    step(sa, sb, 0, j + 1, true, next(sa, 3), std::integral_constant<int, 2 * RUN>{});
-    step(sa, sb, 1, j + 2, false, next(sa, 4), std::integral_constant<int, RUN>{});
+    step(sa, sb, 0, j + (H0 >> 1), H0 & 1, next(sa, SLOTS - 2), std::integral_constant<int, (SLOTS - 3) * RUN>{});
+    step(sa, sb, 1, j + ((H0 + 1) >> 1), (H0 + 1) & 1, next(sa, SLOTS - 1),
+         std::integral_constant<int, (SLOTS - 4) * RUN>{});
     sa = next(sa, 2);
   }
   for (; j < np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
-    int h = 2 * j + 3, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
-    step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, 2 * RUN>{});
-    h = 2 * j + 4, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
-    step(sa, sb, 1, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, RUN>{});
+    int h = 2 * j + H0, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
+    step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, (SLOTS - 3) * RUN>{});
+    h = 2 * j + H0 + 1, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
+    step(sa, sb, 1, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, (SLOTS - 4) * RUN>{});
     sa = next(sa, 2);
   }
   if (wm == 0) {
@@ -920,12 +923,14 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const bool mapped = p.ep.glu || p.b_head_w > 0;
   if (mapped && p.row_r != nullptr) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER) {
-    if constexpr (BM == 256 && BN == 256 && WAVES_M == 2 && WAVES_N == 4 && SCHED == 1) {
-      if (p.K % 64 == 0) {  // whole K pairs: 128-byte LDS rows
+    if constexpr (BM == BN && (BM == 256 || BM == 128) && WAVES_M == 2 && WAVES_N == 4 && SCHED == 1) {
+      constexpr int S = BM == 256 ? 5 : 10;  // 160 KB of halves
+      if (p.K % 64 == 0) {                  // whole K pairs: 128-byte LDS rows
         if (mapped)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<false, true>), grid, block, 0, stream, p, tiles_m, tiles_n, group_m);
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, S, false, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
+                             group_m);
         else
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<false, false>), grid, block, 0, stream, p, tiles_m, tiles_n,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, S, false, false>), grid, block, 0, stream, p, tiles_m, tiles_n,
                              group_m);
         return hipGetLastError();
       }
@@ -955,12 +960,10 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   const int group_m = tiles_m < 4 ? tiles_m : 4;
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
   if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
-  if constexpr (BM == 256 && BN == 256) {
-    if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
-      hipLaunchKernelGGL((gemm_nt_pair_kernel<true, false>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
-                         tiles_m, tiles_n, group_m);
-      return hipGetLastError();
-    }
+  if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
+    hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n), dim3(512),
+                       0, stream, p, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
                      tiles_m, tiles_n, group_m);
@@ -1005,7 +1008,7 @@ hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t str
   switch (tile) {
     case TILE_256x256: return launch_tile<256, 256, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_256x128: return launch_tile<256, 128, 2, 2, 6>(p, path, stream);
-    case TILE_128x128: return launch_tile<128, 128, 2, 2, 5>(p, path, stream);
+    case TILE_128x128: return launch_tile<128, 128, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_128x256: return launch_tile<128, 256, 2, 2, 6>(p, path, stream);
     case TILE_256x224: return launch_tile<256, 224, 4, 1, 5>(p, path, stream);
     case TILE_128x64: return launch_tile<128, 64, 2, 2, 4>(p, path, stream);

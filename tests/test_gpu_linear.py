@@ -184,7 +184,8 @@ def test_empty_input():
 
 def test_buffer_load_span_limit():
     """The direct-to-LDS loads of the eight-wave 256x256 tile go through buffer resources that
-    reach 2^31 - 1 bytes from a tile's first row. At K = 4194272 a full tile's last A and B rows
+    reach 2^31 - 1 bytes from a tile's first row. At K = 4194272 (64-byte rows) and K = 4194240
+    (the largest whole number of 64-wide pairs: 128-byte rows) a full tile's last A and B rows
     sit just inside that reach, so the forced direct-to-LDS path runs with its largest offsets;
     at K = 4194304 they do not: the forced path is refused and the automatic one falls back to
     register staging. Values in {-1, 0, 1} keep every float32 partial sum exact (|sum| < 2^24),
@@ -193,7 +194,7 @@ def test_buffer_load_span_limit():
     rows, cols = [0, 1, 130, 255], [0, 77, 128, 255]
     g = torch.Generator(device="cuda")
     g.manual_seed(991)
-    for K, fits in ((4194272, True), (4194304, False)):
+    for K, fits in ((4194272, True), (4194240, True), (4194304, False)):
         x = torch.randint(-1, 2, (M, K), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
         w = torch.randint(-1, 2, (N, K), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
         tt.set_gemm_tile(0)
@@ -214,16 +215,18 @@ def test_buffer_load_span_limit():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("tile", [0, 2])
 @pytest.mark.parametrize("K", [64, 128, 448, 1344])
-def test_paired_k_rows_tile_integer_exact(K):
-    """The 256x256 tile on whole 64-wide K pairs stages two K steps per 128-byte LDS row: one
-    pair (the prologue's third half reloads the last pair), a few pairs (every issue past the
-    end reloads it), and 21 pairs (the five-slot ring wraps several times). Ragged M and N,
-    a sub-parameter boundary inside the tile, bias, GELU; bit-exact on integer inputs."""
-    tt.set_gemm_tile(0)
+def test_paired_k_rows_tile_integer_exact(tile, K):
+    """The 256x256 and 128x128 tiles on whole 64-wide K pairs stage two K steps per 128-byte
+    LDS row: one pair (the prologue's later halves reload the last pair), a few pairs (every
+    issue past the end reloads it), and 21 pairs (the ring of 5 or 10 halves wraps several
+    times). Ragged M and N, a sub-parameter boundary inside the tile, bias, GELU; bit-exact on
+    integer inputs."""
+    tt.set_gemm_tile(tile)
     tt.set_gemm_path(tt.GEMM_PATH_DMA)
     M, sizes, tp, rank = 301, [300, 76, 76], 2, 1
-    x, w, b, w_r, b_r = _int_inputs(M, K, sizes, tp, rank, 40 + K)
+    x, w, b, w_r, b_r = _int_inputs(M, K, sizes, tp, rank, 40 + K + tile)
     y = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, y_dtype=tt.TP_DTYPE_F32)
     torch.cuda.synchronize()
     assert np.array_equal(host_f32(y), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, out_dtype=oracle.OUT_F32))
