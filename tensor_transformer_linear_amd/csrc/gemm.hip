@@ -1007,9 +1007,9 @@ hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t str
   if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.ep.glu ? 2 * p.N : p.N, p.K);
   switch (tile) {
     case TILE_256x256: return launch_tile<256, 256, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
-    case TILE_256x128: return launch_tile<256, 128, 2, 2, 6>(p, path, stream);
+    case TILE_256x128: return launch_tile<256, 128, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_128x128: return launch_tile<128, 128, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
-    case TILE_128x256: return launch_tile<128, 256, 2, 2, 6>(p, path, stream);
+    case TILE_128x256: return launch_tile<128, 256, 2, 4, 5, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_256x224: return launch_tile<256, 224, 4, 1, 5>(p, path, stream);
     case TILE_128x64: return launch_tile<128, 64, 2, 2, 4>(p, path, stream);
     case TILE_64x64: return launch_tile<64, 64, 2, 2, 4>(p, path, stream);
