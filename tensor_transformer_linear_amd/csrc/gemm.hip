@@ -12,11 +12,13 @@
 //   32-wide K step goes global -> LDS into a ring of stages, several in flight,
 //   through buffer_load_dwordx4 ... lds where a wave's blocks of a stage are
 //   contiguous (one M0 and one scalar K offset serve them all), through
-//   global_load_lds_dwordx4 otherwise. The 256x256 tile runs eight waves in two groups
-//   that ping-pong (one group multiplies while the other reads its next
-//   fragments and issues the next loads); other tiles double-buffer the operand
-//   fragments in registers so the LDS reads of one half-step overlap the MFMAs
-//   of the other;
+//   global_load_lds_dwordx4 otherwise. The 256x256, 256x128, 128x256 and 128x128
+//   tiles run eight waves in two groups that ping-pong (one group multiplies while
+//   the other reads its next fragments and issues the next loads); the square ones
+//   stage two K steps per 128-byte LDS row when K holds whole pairs, so every row
+//   fetch is one full cache line. The other tiles double-buffer the operand
+//   fragments in registers so the LDS reads of one half-step overlap the MFMAs of
+//   the other;
 // * register staging (any K % 8 == 0, and the fused RMSNorm): 64-wide K steps
 //   go global -> registers -> LDS through two stages; the A slab can be
 //   RMS-normalised on its way into LDS.
