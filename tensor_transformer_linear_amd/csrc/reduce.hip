@@ -18,7 +18,9 @@ namespace {
 
 constexpr int RS_THREADS = 256;
 
-// TPC > 0: the rank count is a compile-time constant (loads unrolled); 0: runtime loop.
+// TPC > 0: the rank count is a compile-time constant (loads unrolled); 0: runtime loop. Each
+// partial element is read exactly once: non-temporal loads (26.0 -> 23.9 us per destination
+// on the llama-8B MLP shard).
 template <int TPC>
 __global__ __launch_bounds__(RS_THREADS) void reduce_scatter_kernel(ReduceScatterProblem p) {
   const int64_t id = (int64_t)blockIdx.x * RS_THREADS + threadIdx.x;
@@ -32,13 +34,13 @@ __global__ __launch_bounds__(RS_THREADS) void reduce_scatter_kernel(ReduceScatte
   if constexpr (TPC > 0) {
     f32x4_t v[TPC];
 #pragma unroll
-    for (int r = 0; r < TPC; ++r) v[r] = *reinterpret_cast<const f32x4_t*>(p.part[r] + src);
+    for (int r = 0; r < TPC; ++r) v[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p.part[r] + src));
     s = v[0];
 #pragma unroll
     for (int r = 1; r < TPC; ++r) s += v[r];
   } else {
-    s = *reinterpret_cast<const f32x4_t*>(p.part[0] + src);
-    for (int r = 1; r < p.tp; ++r) s += *reinterpret_cast<const f32x4_t*>(p.part[r] + src);
+    s = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p.part[0] + src));
+    for (int r = 1; r < p.tp; ++r) s += __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p.part[r] + src));
   }
   const int64_t o = i * p.N + c;
   if (p.y_sum != nullptr) *reinterpret_cast<f32x4_t*>(p.y_sum + o) = s;

@@ -6,8 +6,10 @@
 // One workgroup per row. Each thread sums the squares of its 16-byte chunks of the
 // row in float32 (squares of bf16 values are exact in float32); the partial sums
 // are combined in float64 and r is rounded to float32 once. The row is read once
-// from HBM; when the normalised row is requested it is produced in the same pass
-// from registers (rows up to 8192 wide) or from a second, cache-resident read.
+// from HBM (non-temporal loads for the chunks held in registers: 180 -> 175 us on a
+// 32768 x 8192 pass; non-temporal stores of the normalised rows, which the GEMM reads
+// next, measured slower); when the normalised row is requested it is produced in the
+// same pass from registers (rows up to 8192 wide) or from a second, cache-resident read.
 // Workgroup 0 also writes t = bf16(1 + s), which the GEMM applies while staging A.
 #include "common.h"
 #include "kernels.h"
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(RMS_THREADS) void rmsnorm_rows_kernel(const uint16_
   for (int i = 0; i < RMS_HELD; ++i) {
     int c = tid + i * RMS_THREADS;
     if (c < nchunk) {
-      held[i] = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
+      held[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xr + c * 8));
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         float lo = bf16_lo(held[i][w]), hi = bf16_hi(held[i][w]);
