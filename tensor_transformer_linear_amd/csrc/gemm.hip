@@ -751,7 +751,7 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
     voff_a[b] = (uint32_t)(((int64_t)(gm - m0) * p.lda) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
     voff_b[b] = (uint32_t)(((int64_t)(gn - nb_first) * p.ldb) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
   }
-  // Half h (pair h / 2, clamped to the last pair) into slot `slot` (h % 5, or the clamped
+  // Half h (pair h / 2, clamped to the last pair) into slot `slot` (h % S, or the clamped
   // half's slot): A rows for even h, B rows for odd h.
   auto issue_half = [&](int pair, bool b_rows, unsigned slot) {
     lds_byte* base = (lds_byte*)smem + slot * HALF + wave_s * RUN * 1024;
