@@ -14,9 +14,9 @@
 //   contiguous (one M0 and one scalar K offset serve them all), through
 //   global_load_lds_dwordx4 otherwise. The 256x256, 256x128, 128x256 and 128x128
 //   tiles run eight waves in two groups that ping-pong (one group multiplies while
-//   the other reads its next fragments and issues the next loads); the square ones
-//   stage two K steps per 128-byte LDS row when K holds whole pairs, so every row
-//   fetch is one full cache line. The other tiles double-buffer the operand
+//   the other reads its next fragments and issues the next loads) and stage two K
+//   steps per 128-byte LDS row when K holds whole pairs, so every row fetch is one
+//   full cache line. The other tiles double-buffer the operand
 //   fragments in registers so the LDS reads of one half-step overlap the MFMAs of
 //   the other;
 // * register staging (any K % 8 == 0, and the fused RMSNorm): 64-wide K steps
@@ -694,30 +694,42 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_nt_dma_kernel(Gemm
   }
 }
 
-// Ping-pong square tile (256 or 128) on paired K steps. An LDS row holds two consecutive K steps (128
+// Ping-pong tile (256x256, 128x128, 256x128, 128x256) on paired K steps. An LDS row holds two consecutive K steps (128
 // bytes: 64 bf16 or 128 E4M3 values), so the eight lanes that fetch a row of a 1 KB block (8
 // rows) read one whole 128-byte line: half the cache requests of 64-byte rows for the same
 // bytes. The 16-byte chunk index is XORed with bits 1..3 of the row, so the 16 consecutive rows
 // one ds_read_b128 phase reads fall on 16 distinct bank groups (row parity picks the half of
 // the 256-byte bank window).
 //
-// The ring is S slots of one operand's rows of one pair (a "half": 32 KB for 256 rows, 16 KB
-// for 128; S = 5 and 10, 160 KB). Half h is the A rows (h even) or the B rows (h odd) of K pair
-// h / 2 and lives in slot h % S. Memory phase k (the two groups run the same ping-pong as the
+// The ring is S slots, each the size of one operand's rows of one pair (a "half": 32 KB for 256
+// rows, 16 KB for 128; S = 5 for tiles with a 256-row operand, 10 for 128x128: 160 KB). Half h is
+// the A rows (h even) or the B rows (h odd) of K pair h / 2 and lives in slot h % S. Memory phase k (the two groups run the same ping-pong as the
 // 64-byte-row kernel) reads step k from halves 2 (k / 2) and 2 (k / 2) + 1, issues half
 // k + S - 2 into the slot of half k - 2 (which both groups finished reading at step k - 1 at
 // the latest, one barrier earlier), and waits until step k + 1's halves have landed: the
 // halves issued after them are k + 2 .. k + S - 2 for even k and k + 3 .. k + S - 2 for odd
 // k. Halves past the last pair reload the last pair into its own slot (identical bytes), so
-// every phase issues the same loads. Each wave owns a run of BT / 64 A blocks and one of BT /
-// 64 B blocks (one M0 and one buffer resource each).
+// every phase issues the same loads. Each wave owns a run of BM / 64 A blocks and one of BN / 64
+// B blocks (one M0 and one buffer resource each); the waits count each half's own loads.
 __device__ __forceinline__ int pair_off(int row, int lc) { return row * 128 + ((lc ^ ((row >> 1) & 7)) << 4); }
 
-template <int BT, int SLOTS, bool FP8, bool MAPPED>
+// Loads one wave issues for half h + d when h is even (A halves: RA blocks, B halves: RB).
+constexpr int pair_loads(int d, int ra, int rb) { return (d & 1) ? rb : ra; }
+constexpr int pair_wait(int from, int to, int parity, int ra, int rb) {
+  int n = 0;
+  for (int d = from; d <= to; ++d) n += pair_loads(d + parity, ra, rb);
+  return n;
+}
+
+template <int BM, int BN, int SLOTS, bool FP8, bool MAPPED>
 __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int tiles_m, int tiles_n, int group_m) {
-  constexpr int BM = BT, BN = BT, WAVES_M = 2, WAVES_N = 4, WM = BT / 2, WN = BT / 4, FM = WM / 32, FN = WN / 32;
-  constexpr int HALF = BT * 128, RUN = BT / 64;  // a wave's blocks per half
-  static_assert((BT == 256 || BT == 128) && SLOTS >= 4 && (SLOTS - 3) * RUN < 64, "pair ring shape");
+  constexpr int WAVES_M = 2, WAVES_N = 4, WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
+  constexpr int HALF = (BM > BN ? BM : BN) * 128;  // slot size: the larger operand's half
+  constexpr int RA = BM / 64, RB = BN / 64;          // a wave's blocks per A half and per B half
+  // vmcnt after an even step's issue, an odd step's, and the prologue's (see above)
+  constexpr int VM_EVEN = pair_wait(2, SLOTS - 2, 0, RA, RB), VM_ODD = pair_wait(3, SLOTS - 2, 1, RA, RB);
+  constexpr int VM_PRO = pair_wait(2, SLOTS - 3, 0, RA, RB);
+  static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && SLOTS >= 4 && VM_EVEN < 64, "pair ring shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SLOTS * HALF];
   static_assert(SLOTS * HALF >= WAVES_M * 32 * (BN + 4) * 4, "the output stage reuses the ring");
 
@@ -741,27 +753,35 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.A) + (int64_t)m0 * p.lda * ESZ;
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.B) + (int64_t)nb_first * p.ldb * ESZ;
   const __amdgpu_buffer_rsrc_t rsrc_a = buf_rsrc(abase), rsrc_b = buf_rsrc(bbase);
-  uint32_t voff_a[RUN], voff_b[RUN];
+  uint32_t voff_a[RA], voff_b[RB];
 #pragma unroll
-  for (int b = 0; b < RUN; ++b) {
-    const int row = (RUN * wave_s + b) * 8 + (lane >> 3);
+  for (int b = 0; b < RA; ++b) {
+    const int row = (RA * wave_s + b) * 8 + (lane >> 3);
     const int lc = (lane & 7) ^ ((row >> 1) & 7);
     const int gm = min(m0 + row, M - 1);
-    const int gn = tile_b_row<BN, MAPPED>(p, n0, row);
     voff_a[b] = (uint32_t)(((int64_t)(gm - m0) * p.lda) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int row = (RB * wave_s + b) * 8 + (lane >> 3);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
+    const int gn = tile_b_row<BN, MAPPED>(p, n0, row);
     voff_b[b] = (uint32_t)(((int64_t)(gn - nb_first) * p.ldb) * ESZ + lc * 16 + BUF_BACKOFF - b * 1024);
   }
   // Half h (pair h / 2, clamped to the last pair) into slot `slot` (h % S, or the clamped
   // half's slot): A rows for even h, B rows for odd h.
   auto issue_half = [&](int pair, bool b_rows, unsigned slot) {
-    lds_byte* base = (lds_byte*)smem + slot * HALF + wave_s * RUN * 1024;
-    static_for<RUN>([&](auto b) {
-      constexpr int bi = decltype(b)::value;
-      if (b_rows)
-        buf_load16<bi * 1024>(rsrc_b, voff_b[bi], pair * 128, base);
-      else
-        buf_load16<bi * 1024>(rsrc_a, voff_a[bi], pair * 128, base);
-    });
+    lds_byte* base = (lds_byte*)smem + slot * HALF;
+    if (b_rows)
+      static_for<RB>([&](auto b) {
+        constexpr int bi = decltype(b)::value;
+        buf_load16<bi * 1024>(rsrc_b, voff_b[bi], pair * 128, base + wave_s * RB * 1024);
+      });
+    else
+      static_for<RA>([&](auto b) {
+        constexpr int bi = decltype(b)::value;
+        buf_load16<bi * 1024>(rsrc_a, voff_a[bi], pair * 128, base + wave_s * RA * 1024);
+      });
   };
   auto issue_clamped = [&](int h) {
     const int hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
@@ -835,7 +855,7 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   // phase behind group 0 (an extra barrier at its start, one at group 0's end).
 #pragma unroll
   for (int h = 0; h < SLOTS - 2; ++h) issue_clamped(h);
-  wait_barrier(std::integral_constant<int, (SLOTS - 4) * RUN>{}, std::integral_constant<int, 15>{});
+  wait_barrier(std::integral_constant<int, VM_PRO>{}, std::integral_constant<int, 15>{});
   if (wm == 1) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -871,17 +891,16 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   int j = 0;
   for (; 2 * j + SLOTS <= 2 * np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
-    step(sa, sb, 0, j + (H0 >> 1), H0 & 1, next(sa, SLOTS - 2), std::integral_constant<int, (SLOTS - 3) * RUN>{});
-    step(sa, sb, 1, j + ((H0 + 1) >> 1), (H0 + 1) & 1, next(sa, SLOTS - 1),
-         std::integral_constant<int, (SLOTS - 4) * RUN>{});
+    step(sa, sb, 0, j + (H0 >> 1), H0 & 1, next(sa, SLOTS - 2), std::integral_constant<int, VM_EVEN>{});
+    step(sa, sb, 1, j + ((H0 + 1) >> 1), (H0 + 1) & 1, next(sa, SLOTS - 1), std::integral_constant<int, VM_ODD>{});
     sa = next(sa, 2);
   }
   for (; j < np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
     int h = 2 * j + H0, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
-    step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, (SLOTS - 3) * RUN>{});
+    step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, VM_EVEN>{});
     h = 2 * j + H0 + 1, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
-    step(sa, sb, 1, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, (SLOTS - 4) * RUN>{});
+    step(sa, sb, 1, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, VM_ODD>{});
     sa = next(sa, 2);
   }
   if (wm == 0) {
@@ -925,15 +944,16 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
   const bool mapped = p.ep.glu || p.b_head_w > 0;
   if (mapped && p.row_r != nullptr) return hipErrorInvalidValue;
   if (dma_ok && path != GEMM_PATH_REGISTER) {
-    if constexpr (BM == BN && (BM == 256 || BM == 128) && WAVES_M == 2 && WAVES_N == 4 && SCHED == 1) {
-      constexpr int S = BM == 256 ? 5 : 10;  // 160 KB of halves
-      if (p.K % 64 == 0) {                  // whole K pairs: 128-byte LDS rows
+    if constexpr ((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && WAVES_M == 2 && WAVES_N == 4 &&
+                  SCHED == 1) {
+      constexpr int S = BM == 256 || BN == 256 ? 5 : 10;  // 160 KB of halves
+      if (p.K % 64 == 0) {                               // whole K pairs: 128-byte LDS rows
         if (mapped)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, S, false, true>), grid, block, 0, stream, p, tiles_m, tiles_n,
-                             group_m);
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, true>), grid, block, 0, stream, p, tiles_m,
+                             tiles_n, group_m);
         else
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, S, false, false>), grid, block, 0, stream, p, tiles_m, tiles_n,
-                             group_m);
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false>), grid, block, 0, stream, p, tiles_m,
+                             tiles_n, group_m);
         return hipGetLastError();
       }
     }
@@ -963,8 +983,8 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
   if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
   if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
-    hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n), dim3(512),
-                       0, stream, p, tiles_m, tiles_n, group_m);
+    hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n),
+                       dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,

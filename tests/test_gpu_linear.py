@@ -215,14 +215,15 @@ def test_buffer_load_span_limit():
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("tile", [0, 2])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
 @pytest.mark.parametrize("K", [64, 128, 448, 1344])
 def test_paired_k_rows_tile_integer_exact(tile, K):
-    """The 256x256 and 128x128 tiles on whole 64-wide K pairs stage two K steps per 128-byte
-    LDS row: one pair (the prologue's later halves reload the last pair), a few pairs (every
-    issue past the end reloads it), and 21 pairs (the ring of 5 or 10 halves wraps several
-    times). Ragged M and N, a sub-parameter boundary inside the tile, bias, GELU; bit-exact on
-    integer inputs."""
+    """The eight-wave tiles (256x256, 256x128, 128x128, 128x256) on whole 64-wide K pairs
+    stage two K steps per 128-byte LDS row: one pair (the prologue's later halves reload the
+    last pair), a few pairs (every issue past the end reloads it), and 21 pairs (the ring of 5
+    or 10 halves wraps several times; unequal A and B halves for the non-square tiles). Ragged
+    M and N, a sub-parameter boundary inside the tile, bias, GELU; bit-exact on integer
+    inputs."""
     tt.set_gemm_tile(tile)
     tt.set_gemm_path(tt.GEMM_PATH_DMA)
     M, sizes, tp, rank = 301, [300, 76, 76], 2, 1
