@@ -94,6 +94,47 @@ __device__ __forceinline__ int64_t head_out_col(const GemmEpilogue& ep, int c) {
   return (int64_t)h * ep.c_head_pitch + ep.c_head_off + (c - h * ep.c_head_w);
 }
 
+// The output is written once and not read back by the kernel: its whole-chunk stores are
+// non-temporal (measured 0.5-2% faster than ordinary stores on the GEMM shapes).
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_nt;
+
+// Output columns col .. col + 3 of an epilogue chunk: the segment shift of the first, whether
+// all four share its segment and lie below N, and their column scales and bias. Indices past N
+// clamp to column N - 1 (N >= 1), so the loads need no per-element branch and issue together;
+// values past N are never stored.
+struct ChunkCols {
+  int col, d;
+  bool whole;
+  float cs[4], bs[4];
+};
+__device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col, int N) {
+  ChunkCols c;
+  c.col = col;
+  c.d = 0;
+  int seg_end = N;
+  for (int sg = 0; sg < ep.n_seg; ++sg)
+    if (col < ep.seg_end[sg]) {
+      c.d = ep.seg_delta[sg];
+      seg_end = ep.seg_end[sg];
+      break;
+    }
+  c.whole = col + 4 <= seg_end && col + 4 <= N;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c.cs[e] = 1.0f;
+    c.bs[e] = 0.0f;
+  }
+  if (ep.row_scale != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c.cs[e] = ep.col_scale[min(col + e, N - 1)];
+  }
+  if (ep.bias != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c.bs[e] = bf16_to_f32(ep.bias[min(col + e, N - 1)]);
+  }
+  return c;
+}
+
 // Output stage of a BM x BN tile, one 32-row band of every wave at a time. In a 32x32
 // accumulator block, lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of
 // its sixteen values v. Each wave parks its band (32 rows x WN columns) in LDS; the
@@ -113,7 +154,27 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   constexpr int C4 = BN / 4;                         // four-column chunks per staged row
   constexpr int CHUNKS = SROWS * C4;
   static_assert(CHUNKS % NT == 0, "band chunks must divide evenly over the workgroup");
+  constexpr int Q = CHUNKS / NT;                     // chunks per thread per band
+  // A thread's chunk column c4 = (tid + q NT) % C4 is the same in every pass when NT is a
+  // multiple of C4 (every eight-wave tile): its segment, column scales and bias are then
+  // fetched once per tile.
+  constexpr bool FIXED_COL = NT % C4 == 0;
+  ChunkCols fixed_cols{};
+  if constexpr (FIXED_COL)
+    if (!(MAPPED && ep.glu)) fixed_cols = chunk_cols(ep, n0 + (tid % C4) * 4, N);
   static_for<FM>([&](auto i) {
+    // this band's row scales (eight-wave tiles), fetched before the staging so their latency
+    // overlaps it; other tiles load each chunk's row scale where it is used
+    float rsv[FIXED_COL ? Q : 1];
+    if constexpr (FIXED_COL) {
+      if (!(MAPPED && ep.glu) && ep.row_scale != nullptr) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const int sr = (tid + q * NT) / C4;
+          rsv[q] = ep.row_scale[min(m0 + (sr >> 5) * WM + i * 32 + (sr & 31), M - 1)];
+        }
+      }
+    }
     static_for<FN>([&](auto j) {
       static_for<16>([&](auto v) {
         constexpr int vv = v;
@@ -143,10 +204,8 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
           const bool whole = col + 4 <= N && (ep.c_head_w <= 0 || in_head + 4 <= ep.c_head_w);
           uint16_t* c = out + head_out_col(ep, col);
           if (whole && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
-            uint2 pk;
-            pk.x = pack_bf16x2(y[0], y[1]);
-            pk.y = pack_bf16x2(y[2], y[3]);
-            *reinterpret_cast<uint2*>(c) = pk;
+            const u32x2_nt pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_nt*>(c));
           } else {
             for (int e = 0; e < 4 && col + e < N; ++e) out[head_out_col(ep, col + e)] = f32_to_bf16(y[e]);
           }
@@ -155,31 +214,23 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
       __syncthreads();
       return;
     }
-    for (int q = 0; q < CHUNKS / NT; ++q) {
+    for (int q = 0; q < Q; ++q) {  // (unrolling this copies the kernel arguments to scratch)
       const int id = tid + q * NT;
       const int sr = id / C4, c4 = id - sr * C4;
       const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
-      const int col = n0 + c4 * 4;
+      // output column of the chunk's first column, and whether all four share its segment
+      const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols(ep, n0 + c4 * 4, N);
+      const int col = cc.col, d = cc.d;
+      const bool whole = cc.whole;
       if (row < M && col < N) {
         f32x4_t val = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4);
-        // output column of the chunk's first column, and whether all four share its segment
-        int d = 0, seg_end = N;
-        for (int sg = 0; sg < ep.n_seg; ++sg)
-          if (col < ep.seg_end[sg]) {
-            d = ep.seg_delta[sg];
-            seg_end = ep.seg_end[sg];
-            break;
-          }
-        const bool whole = col + 4 <= seg_end && col + 4 <= N;
         if (ep.row_scale != nullptr) {  // fp8: dequantise the product
-          const float rs = ep.row_scale[row];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (col + e < N) val[e] *= rs * ep.col_scale[col + e];
+          for (int e = 0; e < 4; ++e) val[e] *= (FIXED_COL ? rsv[FIXED_COL ? q : 0] : ep.row_scale[row]) * cc.cs[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (ep.bias != nullptr && col + e < N) val[e] += bf16_to_f32(ep.bias[col + e]);
+          if (ep.bias != nullptr) val[e] += cc.bs[e];
           if (ep.act == TP_ACT_GELU_ERF) val[e] = gelu_erf(val[e]);
         }
         const int64_t base = (int64_t)row * ep.ldc;
@@ -188,7 +239,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
           if (whole && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
             f32x4_t* c4p = reinterpret_cast<f32x4_t*>(c);
             if (ep.accumulate) val += *c4p;
-            *c4p = val;
+            __builtin_nontemporal_store(val, c4p);
           } else {
             for (int e = 0; e < 4 && col + e < N; ++e) {
               int de = d;
@@ -204,10 +255,8 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
         } else {
           uint16_t* c = reinterpret_cast<uint16_t*>(ep.C) + base + col + d;
           if (whole && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
-            uint2 pk;
-            pk.x = pack_bf16x2(val[0], val[1]);
-            pk.y = pack_bf16x2(val[2], val[3]);
-            *reinterpret_cast<uint2*>(c) = pk;
+            const u32x2_nt pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_nt*>(c));
           } else {
             for (int e = 0; e < 4 && col + e < N; ++e) {
               int de = d;
@@ -1004,6 +1053,7 @@ hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
   if (!p.fp8 || p.K % 64 != 0 || p.lda % 16 != 0 || p.ldb % 16 != 0 || p.row_r != nullptr || p.ep.glu ||
       p.b_head_w > 0)
     return hipErrorInvalidValue;
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;  // nothing to write
   if (tile == TILE_AUTO) tile = gemm_fp8_pick_tile(p.M, p.N, p.K);
   switch (tile) {
     case TILE_256x256: return launch_tile_fp8<256, 256>(p, stream);
@@ -1033,6 +1083,7 @@ int gemm_pick_tile(int M, int N, int K) {
 }
 
 hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t stream) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;  // nothing to write (the epilogue clamps to row M - 1, column N - 1)
   if (tile == TILE_AUTO) tile = gemm_pick_tile(p.M, p.ep.glu ? 2 * p.N : p.N, p.K);
   switch (tile) {
     case TILE_256x256: return launch_tile<256, 256, 2, 4, 4, 1>(p, path, stream);  // 8 waves, ping-pong
