@@ -94,6 +94,13 @@ __device__ __forceinline__ int64_t head_out_col(const GemmEpilogue& ep, int c) {
   return (int64_t)h * ep.c_head_pitch + ep.c_head_off + (c - h * ep.c_head_w);
 }
 
+// Output-stage modes. A kernel built for one of the fixed modes carries only that path: the
+// generic stage's code (GELU, float32 and accumulate, fp8 scales, per-element fallbacks)
+// measured 18 us of fixed cost per launch on the 32768 x 3072 GEMM when it is not needed.
+constexpr int EPI_GENERIC = 0;    // every mode decided at run time
+constexpr int EPI_BF16 = 1;       // bf16 output, no activation, no fp8 scales (bias as given)
+constexpr int EPI_BF16_GELU = 2;  // bf16 output, exact GELU, no fp8 scales (bias as given)
+
 // The output is written once and not read back by the kernel: its whole-chunk stores are
 // non-temporal (measured 0.5-2% faster than ordinary stores on the GEMM shapes).
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_nt;
@@ -107,6 +114,7 @@ struct ChunkCols {
   bool whole;
   float cs[4], bs[4];
 };
+template <bool MAY_SCALE>
 __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col, int N) {
   ChunkCols c;
   c.col = col;
@@ -124,7 +132,7 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
     c.cs[e] = 1.0f;
     c.bs[e] = 0.0f;
   }
-  if (ep.row_scale != nullptr) {
+  if (MAY_SCALE && ep.row_scale != nullptr) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) c.cs[e] = ep.col_scale[min(col + e, N - 1)];
   }
@@ -141,7 +149,7 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
 // workgroup then reads the staged band back four consecutive columns per thread and
 // finishes them: bias, GELU, one rounding, the column remap, and a coalesced store (or a
 // float32 add). `smem` must hold WAVES_M * 32 * (BN + 4) floats and be free.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool MAPPED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool MAPPED, int EPI = EPI_GENERIC>
 __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (&acc)[FM][FN], unsigned char* smem,
                                                 int m0, int n0, int wm, int wn, int lane, int tid) {
   constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -151,6 +159,11 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   constexpr int SROWS = WAVES_M * 32;                // staged rows per band
   float* stage = reinterpret_cast<float*>(smem);
   const GemmEpilogue& ep = p.ep;
+  // the epilogue's modes: runtime for EPI_GENERIC, fixed at compile time otherwise
+  constexpr bool GEN = EPI == EPI_GENERIC;
+  const bool scaled = GEN && ep.row_scale != nullptr;
+  const bool gelu = GEN ? ep.act == TP_ACT_GELU_ERF : EPI == EPI_BF16_GELU;
+  const bool out_f32 = GEN && ep.out_f32 != 0;
   constexpr int C4 = BN / 4;                         // four-column chunks per staged row
   constexpr int CHUNKS = SROWS * C4;
   static_assert(CHUNKS % NT == 0, "band chunks must divide evenly over the workgroup");
@@ -161,13 +174,13 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   constexpr bool FIXED_COL = NT % C4 == 0;
   ChunkCols fixed_cols{};
   if constexpr (FIXED_COL)
-    if (!(MAPPED && ep.glu)) fixed_cols = chunk_cols(ep, n0 + (tid % C4) * 4, N);
+    if (!(MAPPED && ep.glu)) fixed_cols = chunk_cols<GEN>(ep, n0 + (tid % C4) * 4, N);
   static_for<FM>([&](auto i) {
     // this band's row scales (eight-wave tiles), fetched before the staging so their latency
     // overlaps it; other tiles load each chunk's row scale where it is used
     float rsv[FIXED_COL ? Q : 1];
     if constexpr (FIXED_COL) {
-      if (!(MAPPED && ep.glu) && ep.row_scale != nullptr) {
+      if (!(MAPPED && ep.glu) && scaled) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
           const int sr = (tid + q * NT) / C4;
@@ -219,22 +232,22 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
       const int sr = id / C4, c4 = id - sr * C4;
       const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
       // output column of the chunk's first column, and whether all four share its segment
-      const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols(ep, n0 + c4 * 4, N);
+      const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols<GEN>(ep, n0 + c4 * 4, N);
       const int col = cc.col, d = cc.d;
       const bool whole = cc.whole;
       if (row < M && col < N) {
         f32x4_t val = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4);
-        if (ep.row_scale != nullptr) {  // fp8: dequantise the product
+        if (scaled) {  // fp8: dequantise the product
 #pragma unroll
           for (int e = 0; e < 4; ++e) val[e] *= (FIXED_COL ? rsv[FIXED_COL ? q : 0] : ep.row_scale[row]) * cc.cs[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (ep.bias != nullptr) val[e] += cc.bs[e];
-          if (ep.act == TP_ACT_GELU_ERF) val[e] = gelu_erf(val[e]);
+          if (gelu) val[e] = gelu_erf(val[e]);
         }
         const int64_t base = (int64_t)row * ep.ldc;
-        if (ep.out_f32) {
+        if (out_f32) {
           float* c = reinterpret_cast<float*>(ep.C) + base + col + d;
           if (whole && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
             f32x4_t* c4p = reinterpret_cast<f32x4_t*>(c);
@@ -770,7 +783,7 @@ constexpr int pair_wait(int from, int to, int parity, int ra, int rb) {
   return n;
 }
 
-template <int BM, int BN, int SLOTS, bool FP8, bool MAPPED>
+template <int BM, int BN, int SLOTS, bool FP8, bool MAPPED, int EPI = EPI_GENERIC>
 __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int tiles_m, int tiles_n, int group_m) {
   constexpr int WAVES_M = 2, WAVES_N = 4, WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
   constexpr int HALF = (BM > BN ? BM : BN) * 128;  // slot size: the larger operand's half
@@ -957,7 +970,15 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+  gemm_store_tile<BM, BN, WAVES_M, WAVES_N, FM, FN, MAPPED, EPI>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
+// The output-stage mode a launch can be built for (EPI_GENERIC when no fixed mode covers it).
+static int epilogue_mode(const GemmEpilogue& ep) {
+  if (ep.out_f32 || ep.row_scale != nullptr || ep.glu || ep.c_head_w > 0) return EPI_GENERIC;
+  if (ep.act == TP_ACT_NONE) return EPI_BF16;
+  if (ep.act == TP_ACT_GELU_ERF) return EPI_BF16_GELU;
+  return EPI_GENERIC;
 }
 
 // Whether every buffer-loaded byte of a BM x BN tile lies within the 2^31 - 1 bytes a buffer
@@ -1000,6 +1021,12 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
         if (mapped)
           hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, true>), grid, block, 0, stream, p, tiles_m,
                              tiles_n, group_m);
+        else if (epilogue_mode(p.ep) == EPI_BF16)
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16>), grid, block, 0, stream, p,
+                             tiles_m, tiles_n, group_m);
+        else if (epilogue_mode(p.ep) == EPI_BF16_GELU)
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16_GELU>), grid, block, 0, stream,
+                             p, tiles_m, tiles_n, group_m);
         else
           hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false>), grid, block, 0, stream, p, tiles_m,
                              tiles_n, group_m);

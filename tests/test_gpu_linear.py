@@ -234,3 +234,9 @@ def test_paired_k_rows_tile_integer_exact(tile, K):
     yg = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, act=tt.TP_ACT_GELU_ERF)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(yg), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=tt.TP_ACT_GELU_ERF))
+    # bf16 output without activation, with and without bias (the kernels' bf16-only output stage)
+    for bias_r in (b_r, None):
+        yb = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), None if bias_r is None else dev_bf16(bias_r),
+                                 sizes, tp, rank)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(yb), oracle.column_linear(x, w_r, bias_r, sizes, tp, rank))
