@@ -100,10 +100,26 @@ __device__ __forceinline__ int64_t head_out_col(const GemmEpilogue& ep, int c) {
 constexpr int EPI_GENERIC = 0;    // every mode decided at run time
 constexpr int EPI_BF16 = 1;       // bf16 output, no activation, no fp8 scales (bias as given)
 constexpr int EPI_BF16_GELU = 2;  // bf16 output, exact GELU, no fp8 scales (bias as given)
+constexpr int EPI_FP8_BF16 = 3;   // bf16 output, fp8 row and channel scales, no activation (bias as given)
 
 // The output is written once and not read back by the kernel: its whole-chunk stores are
 // non-temporal (measured 0.5-2% faster than ordinary stores on the GEMM shapes).
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_nt;
+
+// The segment holding local column c: the shift and end of the first segment that ends past
+// it, or `none`. Every index is a constant (the loop runs backwards over all TP_MAX_SUBPARAMS
+// slots, so the first match is the one kept): a loop-variable index into the kernel argument's
+// arrays makes the compiler copy the whole argument block to scratch.
+struct SegHit {
+  int delta, end;
+};
+__device__ __forceinline__ SegHit seg_of(const GemmEpilogue& ep, int c, SegHit none) {
+  SegHit h = none;
+#pragma unroll
+  for (int sg = TP_MAX_SUBPARAMS - 1; sg >= 0; --sg)
+    if (sg < ep.n_seg && c < ep.seg_end[sg]) h = SegHit{ep.seg_delta[sg], ep.seg_end[sg]};
+  return h;
+}
 
 // Output columns col .. col + 3 of an epilogue chunk: the segment shift of the first, whether
 // all four share its segment and lie below N, and their column scales and bias. Indices past N
@@ -119,14 +135,9 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
   ChunkCols c;
   c.col = col;
   c.d = 0;
-  int seg_end = N;
-  for (int sg = 0; sg < ep.n_seg; ++sg)
-    if (col < ep.seg_end[sg]) {
-      c.d = ep.seg_delta[sg];
-      seg_end = ep.seg_end[sg];
-      break;
-    }
-  c.whole = col + 4 <= seg_end && col + 4 <= N;
+  const SegHit h = seg_of(ep, col, {0, N});
+  c.d = h.delta;
+  c.whole = col + 4 <= h.end && col + 4 <= N;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     c.cs[e] = 1.0f;
@@ -161,7 +172,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   const GemmEpilogue& ep = p.ep;
   // the epilogue's modes: runtime for EPI_GENERIC, fixed at compile time otherwise
   constexpr bool GEN = EPI == EPI_GENERIC;
-  const bool scaled = GEN && ep.row_scale != nullptr;
+  const bool scaled = GEN ? ep.row_scale != nullptr : EPI == EPI_FP8_BF16;
   const bool gelu = GEN ? ep.act == TP_ACT_GELU_ERF : EPI == EPI_BF16_GELU;
   const bool out_f32 = GEN && ep.out_f32 != 0;
   constexpr int C4 = BN / 4;                         // four-column chunks per staged row
@@ -174,7 +185,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   constexpr bool FIXED_COL = NT % C4 == 0;
   ChunkCols fixed_cols{};
   if constexpr (FIXED_COL)
-    if (!(MAPPED && ep.glu)) fixed_cols = chunk_cols<GEN>(ep, n0 + (tid % C4) * 4, N);
+    if (!(MAPPED && ep.glu)) fixed_cols = chunk_cols<GEN || EPI == EPI_FP8_BF16>(ep, n0 + (tid % C4) * 4, N);
   static_for<FM>([&](auto i) {
     // this band's row scales (eight-wave tiles), fetched before the staging so their latency
     // overlaps it; other tiles load each chunk's row scale where it is used
@@ -227,59 +238,71 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
       __syncthreads();
       return;
     }
-    for (int q = 0; q < Q; ++q) {  // (unrolling this copies the kernel arguments to scratch)
+    // Whole, aligned chunks are finished in this loop. A chunk that crosses a segment end or the
+    // last column, or whose output is misaligned, is left to the element-wise pass below, which
+    // keeps that rare path's code out of the unrolled loop.
+    auto finish = [&](f32x4_t val, float rs, const ChunkCols& cc) {
+      if (scaled) {  // fp8: dequantise the product
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] *= rs * cc.cs[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (ep.bias != nullptr) val[e] += cc.bs[e];
+        if (gelu) val[e] = gelu_erf(val[e]);
+      }
+      return val;
+    };
+    auto vector_ok = [&](const ChunkCols& cc, int64_t off) {
+      const uintptr_t a = out_f32 ? reinterpret_cast<uintptr_t>(reinterpret_cast<float*>(ep.C) + off)
+                                  : reinterpret_cast<uintptr_t>(reinterpret_cast<uint16_t*>(ep.C) + off);
+      return cc.whole && (a & (out_f32 ? 15 : 7)) == 0;
+    };
+    bool partial = false;
+    for (int q = 0; q < Q; ++q) {
       const int id = tid + q * NT;
       const int sr = id / C4, c4 = id - sr * C4;
       const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
       // output column of the chunk's first column, and whether all four share its segment
-      const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols<GEN>(ep, n0 + c4 * 4, N);
-      const int col = cc.col, d = cc.d;
-      const bool whole = cc.whole;
-      if (row < M && col < N) {
-        f32x4_t val = *reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4);
-        if (scaled) {  // fp8: dequantise the product
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] *= (FIXED_COL ? rsv[FIXED_COL ? q : 0] : ep.row_scale[row]) * cc.cs[e];
+      const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols<GEN || EPI == EPI_FP8_BF16>(ep, n0 + c4 * 4, N);
+      if (row < M && cc.col < N) {
+        const int64_t off = (int64_t)row * ep.ldc + cc.col + cc.d;
+        if (!vector_ok(cc, off)) {
+          partial = true;
+          continue;
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (ep.bias != nullptr) val[e] += cc.bs[e];
-          if (gelu) val[e] = gelu_erf(val[e]);
-        }
-        const int64_t base = (int64_t)row * ep.ldc;
+        const float rs = scaled ? (FIXED_COL ? rsv[FIXED_COL ? q : 0] : ep.row_scale[row]) : 1.0f;
+        f32x4_t val = finish(*reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4), rs, cc);
         if (out_f32) {
-          float* c = reinterpret_cast<float*>(ep.C) + base + col + d;
-          if (whole && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
-            f32x4_t* c4p = reinterpret_cast<f32x4_t*>(c);
-            if (ep.accumulate) val += *c4p;
-            __builtin_nontemporal_store(val, c4p);
-          } else {
-            for (int e = 0; e < 4 && col + e < N; ++e) {
-              int de = d;
-              for (int sg = 0; sg < ep.n_seg; ++sg)
-                if (col + e < ep.seg_end[sg]) {
-                  de = ep.seg_delta[sg];
-                  break;
-                }
-              float* ce = reinterpret_cast<float*>(ep.C) + base + col + e + de;
-              *ce = ep.accumulate ? *ce + val[e] : val[e];
-            }
-          }
+          f32x4_t* c4p = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ep.C) + off);
+          if (ep.accumulate) val += *c4p;
+          __builtin_nontemporal_store(val, c4p);
         } else {
-          uint16_t* c = reinterpret_cast<uint16_t*>(ep.C) + base + col + d;
-          if (whole && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
-            const u32x2_nt pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_nt*>(c));
+          const u32x2_nt pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+          __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_nt*>(reinterpret_cast<uint16_t*>(ep.C) + off));
+        }
+      }
+    }
+    if (partial) {
+#pragma unroll 1
+      for (int q = 0; q < Q; ++q) {
+        const int id = tid + q * NT;
+        const int sr = id / C4, c4 = id - sr * C4;
+        const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+        const ChunkCols cc = FIXED_COL ? fixed_cols : chunk_cols<GEN || EPI == EPI_FP8_BF16>(ep, n0 + c4 * 4, N);
+        const int col = cc.col;
+        if (row >= M || col >= N || vector_ok(cc, (int64_t)row * ep.ldc + col + cc.d)) continue;
+        const f32x4_t val = finish(*reinterpret_cast<const f32x4_t*>(stage + sr * SROW + c4 * 4),
+                                   scaled ? ep.row_scale[row] : 1.0f, cc);
+        const int64_t base = (int64_t)row * ep.ldc;
+#pragma unroll 1
+        for (int e = 0; e < 4 && col + e < N; ++e) {
+          const int de = seg_of(ep, col + e, {cc.d, 0}).delta;
+          if (out_f32) {
+            float* ce = reinterpret_cast<float*>(ep.C) + base + col + e + de;
+            *ce = ep.accumulate ? *ce + val[e] : val[e];
           } else {
-            for (int e = 0; e < 4 && col + e < N; ++e) {
-              int de = d;
-              for (int sg = 0; sg < ep.n_seg; ++sg)
-                if (col + e < ep.seg_end[sg]) {
-                  de = ep.seg_delta[sg];
-                  break;
-                }
-              reinterpret_cast<uint16_t*>(ep.C)[base + col + e + de] = f32_to_bf16(val[e]);
-            }
+            reinterpret_cast<uint16_t*>(ep.C)[base + col + e + de] = f32_to_bf16(val[e]);
           }
         }
       }
@@ -975,7 +998,8 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
 
 // The output-stage mode a launch can be built for (EPI_GENERIC when no fixed mode covers it).
 static int epilogue_mode(const GemmEpilogue& ep) {
-  if (ep.out_f32 || ep.row_scale != nullptr || ep.glu || ep.c_head_w > 0) return EPI_GENERIC;
+  if (ep.out_f32 || ep.glu || ep.c_head_w > 0) return EPI_GENERIC;
+  if (ep.row_scale != nullptr) return ep.act == TP_ACT_NONE ? EPI_FP8_BF16 : EPI_GENERIC;
   if (ep.act == TP_ACT_NONE) return EPI_BF16;
   if (ep.act == TP_ACT_GELU_ERF) return EPI_BF16_GELU;
   return EPI_GENERIC;
@@ -1059,8 +1083,12 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
   if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
   if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
-    hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n),
-                       dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
+    if (epilogue_mode(p.ep) == EPI_FP8_BF16)
+      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false, EPI_FP8_BF16>),
+                         dim3(tiles_m * tiles_n), dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
+    else
+      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n),
+                         dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
