@@ -1147,7 +1147,7 @@ hipError_t launch_gemm(const GemmProblem& p, int tile, int path, hipStream_t str
     case TILE_128x256: return launch_tile<128, 256, 2, 4, 5, 1>(p, path, stream);  // 8 waves, ping-pong
     case TILE_256x224: return launch_tile<256, 224, 4, 1, 5>(p, path, stream);
     case TILE_128x64: return launch_tile<128, 64, 2, 2, 4>(p, path, stream);
-    case TILE_64x64: return launch_tile<64, 64, 2, 2, 4>(p, path, stream);
+    case TILE_64x64: return launch_tile<64, 64, 2, 2, 8>(p, path, stream);  // 8 stages: short-K launches keep every K step in flight
     default: return hipErrorInvalidValue;
   }
 }
