@@ -49,8 +49,9 @@ constexpr int LM_FIN_THREADS = 256;
 struct LmShape {
   int G, W, P, KS;
 };
+// (Every shape fits the register file at its wave count: {8, 8, 4, 2} spilled in its E4M3 build.)
 constexpr LmShape kLmShapes[] = {{4, 8, 8, 1}, {2, 8, 8, 1}, {4, 4, 8, 1}, {2, 4, 8, 1},
-                                 {4, 8, 4, 1}, {1, 8, 8, 1}, {8, 8, 4, 2}, {8, 4, 4, 2}};
+                                 {4, 8, 4, 1}, {1, 8, 8, 1}, {4, 8, 4, 2}, {8, 4, 4, 2}};
 constexpr int kLmDmaShape = 8;  // 8, 9: the direct-to-LDS kernel (indices past the table)
 constexpr int kLmDefaultShape = 9;  // LDS ring, 128-byte stages (falls back to 4 for a ragged bf16 K)
 

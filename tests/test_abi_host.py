@@ -339,3 +339,34 @@ def test_reduce_scatter_rejects_oversized_grid():
 def test_reduce_scatter_empty_batch_is_a_no_op():
     assert rs(batch=0) == tt.TP_OK
     assert rs(batch=0, parts=[None, None, None, None], z=None, ys=None, res=None) == tt.TP_OK
+
+
+def _llvm_tool(name):
+    path = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", name)
+    return path if os.path.exists(path) else None
+
+
+def test_no_kernel_uses_scratch(tmp_path):
+    """Every gfx950 kernel in the built library has a zero private segment. A loop-variable
+    index into the kernel argument block, or a register array indexed at run time, makes the
+    compiler place them in per-lane scratch memory: slower, and silent, so it is checked here
+    from the code objects' own metadata."""
+    objdump, readelf = _llvm_tool("llvm-objdump"), _llvm_tool("llvm-readelf")
+    if objdump is None or readelf is None:
+        pytest.skip("ROCm llvm tools not found")
+    copy = tmp_path / "lib.so"
+    copy.write_bytes(open(tt.LIB_PATH, "rb").read())
+    subprocess.run([objdump, "--offloading", str(copy)], cwd=tmp_path, check=True, capture_output=True)
+    sizes = {}
+    for obj in sorted(tmp_path.glob("lib.so.*gfx950*")):
+        notes = subprocess.run([readelf, "--notes", str(obj)], check=True, capture_output=True, text=True).stdout
+        name = None
+        for line in notes.splitlines():
+            m = re.match(r"\s*\.name:\s+(\S+)", line)
+            if m:
+                name = m.group(1)
+            m = re.match(r"\s*\.private_segment_fixed_size:\s+(\d+)", line)
+            if m and name is not None:
+                sizes[name] = int(m.group(1))
+    assert len(sizes) >= 50, f"found only {len(sizes)} kernels in the code objects"
+    assert {k: v for k, v in sizes.items() if v} == {}
