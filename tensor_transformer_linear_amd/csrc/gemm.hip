@@ -101,6 +101,7 @@ constexpr int EPI_GENERIC = 0;    // every mode decided at run time
 constexpr int EPI_BF16 = 1;       // bf16 output, no activation, no fp8 scales (bias as given)
 constexpr int EPI_BF16_GELU = 2;  // bf16 output, exact GELU, no fp8 scales (bias as given)
 constexpr int EPI_FP8_BF16 = 3;   // bf16 output, fp8 row and channel scales, no activation (bias as given)
+constexpr int EPI_F32 = 4;        // float32 output, no activation, no fp8 scales (bias and accumulate as given)
 
 // The output is written once and not read back by the kernel: its whole-chunk stores are
 // non-temporal (measured 0.5-2% faster than ordinary stores on the GEMM shapes).
@@ -174,7 +175,7 @@ __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (
   constexpr bool GEN = EPI == EPI_GENERIC;
   const bool scaled = GEN ? ep.row_scale != nullptr : EPI == EPI_FP8_BF16;
   const bool gelu = GEN ? ep.act == TP_ACT_GELU_ERF : EPI == EPI_BF16_GELU;
-  const bool out_f32 = GEN && ep.out_f32 != 0;
+  const bool out_f32 = GEN ? ep.out_f32 != 0 : EPI == EPI_F32;
   constexpr int C4 = BN / 4;                         // four-column chunks per staged row
   constexpr int CHUNKS = SROWS * C4;
   static_assert(CHUNKS % NT == 0, "band chunks must divide evenly over the workgroup");
@@ -998,7 +999,8 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
 
 // The output-stage mode a launch can be built for (EPI_GENERIC when no fixed mode covers it).
 static int epilogue_mode(const GemmEpilogue& ep) {
-  if (ep.out_f32 || ep.glu || ep.c_head_w > 0) return EPI_GENERIC;
+  if (ep.glu || ep.c_head_w > 0) return EPI_GENERIC;
+  if (ep.out_f32) return ep.act == TP_ACT_NONE && ep.row_scale == nullptr ? EPI_F32 : EPI_GENERIC;
   if (ep.row_scale != nullptr) return ep.act == TP_ACT_NONE ? EPI_FP8_BF16 : EPI_GENERIC;
   if (ep.act == TP_ACT_NONE) return EPI_BF16;
   if (ep.act == TP_ACT_GELU_ERF) return EPI_BF16_GELU;
@@ -1051,6 +1053,9 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
         else if (epilogue_mode(p.ep) == EPI_BF16_GELU)
           hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16_GELU>), grid, block, 0, stream,
                              p, tiles_m, tiles_n, group_m);
+        else if (epilogue_mode(p.ep) == EPI_F32)
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_F32>), grid, block, 0, stream, p,
+                             tiles_m, tiles_n, group_m);
         else
           hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false>), grid, block, 0, stream, p, tiles_m,
                              tiles_n, group_m);
