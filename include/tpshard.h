@@ -348,31 +348,6 @@ TP_API const char* tp_last_error(void);
  */
 TP_API const char* tp_version(void);
 
-/*
- * Tuning and testing hooks (calling thread only).
- * tp_debug_set_gemm_tile   forces the GEMM tile configuration of later calls on this
- *                          thread: -1 restores the automatic choice, 0..6 select
- *                          256x256, 256x128, 128x128, 128x256, 256x224, 128x64, 64x64
- *                          (output rows x columns per workgroup). TP_ERR_INVALID_ARG
- *                          for other values.
- * tp_debug_set_gemm_path   forces the GEMM main loop of later calls on this thread: -1
- *                          automatic, 0 register-staged operands, 1 direct-to-LDS loads
- *                          (needs K % 32 == 0 and no RMSNorm transform; a call that cannot
- *                          use it returns TP_ERR_HIP).
- * tp_debug_set_lm_head_shape forces the LM head's launch shape on this thread: -1 default,
- *                          0..9: register-streaming kernel (16-row weight groups per
- *                          workgroup, waves, K steps per load batch, workgroups splitting
- *                          K) = (4,8,8,1) (2,8,8,1) (4,4,8,1) (2,4,8,1) (4,8,4,1) (1,8,8,1)
- *                          (8,8,4,2) (8,4,4,2); 8, 9 = direct-to-LDS kernel (64 rows, 4
- *                          waves, LDS ring of 64- or 128-byte row stages; a bf16 K that is
- *                          not a multiple of 32 or 64 falls back to shape 4).
- * tp_debug_gemm_pick_tile  the automatic choice for an M x N x K problem (-1 if invalid).
- */
-TP_API int tp_debug_set_gemm_tile(int tile);
-TP_API int tp_debug_set_gemm_path(int path);
-TP_API int tp_debug_set_lm_head_shape(int shape);
-TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
-
 #ifdef __cplusplus
 }
 #endif

@@ -334,16 +334,15 @@ def rmsnorm_column_linear(x_bits, scale_bits, w_shard_bits, bias_shard_bits, sub
 def lm_head_chunks(v_rows: int, max_rows_per_chunk: int):
     """Chunk sizes and row offsets of a vocab shard of ``v_rows`` rows.
 
-    [tt] ``from_model_args``: ``num_splits = ceil(size / max)``, every split but
-    the last has ``min(size, max)`` rows and the last takes the remainder; the
-    splits are laid out back to back, so split ``c`` starts at ``c * max``.
+    [tt] ``from_model_args`` splits the output projection into pieces of at most
+    ``max_rows_per_chunk`` rows, all full except the last, which holds what is left; the
+    pieces sit back to back along the vocab.  So a chunk starts at every multiple of the
+    chunk size below ``v_rows`` and runs to the next multiple or to the end of the shard.
     """
     if max_rows_per_chunk <= 0:
         raise ValueError("max_rows_per_chunk must be positive")
-    n = -(-v_rows // max_rows_per_chunk)
-    sizes = [min(v_rows, max_rows_per_chunk)] * (n - 1)
-    sizes.append(v_rows - sum(sizes))
-    offs = [sum(sizes[:i]) for i in range(n)]
+    offs = list(range(0, v_rows, max_rows_per_chunk))
+    sizes = [min(max_rows_per_chunk, v_rows - o) for o in offs]
     return sizes, offs
 
 

@@ -1,4 +1,8 @@
-"""Build ``libtpshard.so`` (the gfx950 HIP kernels and their C ABI) in-tree with hipcc."""
+"""Build ``libtpshard.so`` (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
+
+The same objects, plus the launch-choice entry points of ``csrc/tuning_abi.hip``, also link
+``libtpshard_tuning.so``, which the tests and measurements use to force a tile, a main loop or
+an LM-head launch shape. The product library does not contain those entry points."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -11,7 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
+TUNING_LIB = os.path.join(PKG, "libtpshard_tuning.so")
 SOURCES = ["tpshard_abi.hip", "gemm.hip", "rmsnorm.hip", "lm_head.hip", "quant.hip", "embed.hip", "reduce.hip"]
+TUNING_SOURCES = ["tuning_abi.hip"]
 ARCH = "gfx950"
 
 
@@ -32,7 +38,8 @@ def flags() -> list[str]:
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every HIP source for gfx950 and link the shared library; returns its path."""
+    """Compile every HIP source for gfx950 and link both shared libraries; returns the product
+    library's path."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
 
@@ -47,13 +54,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + TUNING_SOURCES))
+    n = len(SOURCES)
+    for out, parts in ((LIB, objs[:n]), (TUNING_LIB, objs)):
+        tmp = out + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stderr}")
+        os.replace(tmp, out)
     return LIB
 
 

@@ -1,22 +1,22 @@
 // C ABI of libtpshard: argument checks, shard arithmetic and kernel dispatch.
 //
 // Every check runs on the host before any HIP call; a failed check sets the
-// calling thread's message and returns a status without touching the GPU.
+// calling thread's message and returns a status without touching the GPU. The
+// exported calls hold no state of their own: each passes the automatic launch
+// choices to its internal body (abi_impl.h).
 #include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include "abi_impl.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
 thread_local char g_err[512] = "";
-thread_local int g_tile_override = tpk::TILE_AUTO;
-thread_local int g_path_override = tpk::GEMM_PATH_AUTO;
-thread_local int g_lm_shape_override = -1;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -160,55 +160,32 @@ int resolve_heads(int64_t heads, int64_t padded_heads, int64_t qkv, int64_t ff, 
 
 }  // namespace
 
-extern "C" {
+namespace tpabi {
 
-TP_API const char* tp_last_error(void) { return g_err; }
-
-TP_API const char* tp_version(void) { return "tpshard 0.1 gfx950"; }
-
-TP_API int tp_shard_widths(const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int64_t* width,
-                    int64_t* logical_off, int64_t* local_off, int64_t* shard_total) {
-  Shard sh;
-  int st = resolve_shard(subparam_sizes, n_sub, tp_size, rank, &sh);
-  if (st != TP_OK) return st;
-  for (int i = 0; i < n_sub; ++i) {
-    if (width) width[i] = sh.width[i];
-    if (logical_off) logical_off[i] = sh.logical_off[i];
-    if (local_off) local_off[i] = sh.local_off[i];
-  }
-  if (shard_total) *shard_total = sh.total;
-  return ok();
+int check_tuning(const Tuning& t) {
+  if (t.tile < tpk::TILE_AUTO || t.tile >= tpk::TILE_COUNT) return fail(TP_ERR_INVALID_ARG, "unknown tile %d", t.tile);
+  if (t.path < tpk::GEMM_PATH_AUTO || t.path > tpk::GEMM_PATH_DMA)
+    return fail(TP_ERR_INVALID_ARG, "unknown path %d", t.path);
+  if (t.lm_shape < -1 || t.lm_shape >= tpk::lm_head_shape_count())
+    return fail(TP_ERR_INVALID_ARG, "unknown LM-head shape %d", t.lm_shape);
+  return TP_OK;
 }
 
-TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
-                     const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y, int y_dtype,
-                     int layout, int64_t ldy, void* stream) {
+int column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                  const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y, int y_dtype,
+                  int layout, int64_t ldy, void* stream, const Tuning& tune) {
   tpk::GemmProblem p;
   int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, act, y, y_dtype, layout,
                           ldy, &p);
   if (st != TP_OK) return st;
   if (M == 0) return ok();
-  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_column_linear launch");
+  return hip_status(tpk::launch_gemm(p, tune.tile, tune.path, as_stream(stream)), "tp_column_linear launch");
 }
 
-TP_API int tp_quantize_rows_e4m3(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream) {
-  if (M < 0 || K <= 0) return fail(TP_ERR_INVALID_ARG, "M = %lld, K = %lld: need M >= 0, K > 0", (long long)M, (long long)K);
-  if (M > 0 && (x == nullptr || q == nullptr || scale == nullptr))
-    return fail(TP_ERR_INVALID_ARG, "x, q and scale must be non-NULL");
-  if (M > INT_MAX || K > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and K must fit in 31 bits");
-  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4))
-    return fail(TP_ERR_UNSUPPORTED, "x and q must be 16-byte aligned, scale 4-byte aligned");
-  if (M == 0) return ok();
-  return hip_status(tpk::launch_quantize_rows_e4m3(static_cast<const uint16_t*>(x), (int)M, (int)K,
-                                                   static_cast<uint8_t*>(q), scale, as_stream(stream)),
-                    "tp_quantize_rows_e4m3 launch");
-}
-
-TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
-                                const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
-                                int tp_size, int rank, int act, void* y, int y_dtype, int layout, int64_t ldy,
-                                void* stream) {
+int column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
+                      const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                      int tp_size, int rank, int act, void* y, int y_dtype, int layout, int64_t ldy, void* stream,
+                      const Tuning& tune) {
   tpk::GemmProblem p;
   int st = prepare_column(x_q, M, K, w_q, bias_shard, subparam_sizes, n_sub, tp_size, rank, act, y, y_dtype, layout,
                           ldy, &p);
@@ -221,40 +198,16 @@ TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M
   p.fp8 = 1;
   p.ep.row_scale = x_scale;
   p.ep.col_scale = w_scale;
-  const int tile = g_tile_override == tpk::TILE_256x256 || g_tile_override == tpk::TILE_128x128 ? g_tile_override
-                                                                                                   : tpk::TILE_AUTO;
+  const int tile = tune.tile == tpk::TILE_256x256 || tune.tile == tpk::TILE_128x128 ? tune.tile : tpk::TILE_AUTO;
   const hipError_t e = tpk::launch_gemm_fp8(p, tile, as_stream(stream));
   if (e == hipErrorNotSupported)
     return fail(TP_ERR_UNSUPPORTED, "a tile's operand rows span more than 2^31 - 1 bytes (K = %lld)", (long long)K);
   return hip_status(e, "tp_column_linear_fp8 launch");
 }
 
-TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,
-                              const void* table_shard, int64_t E, void* out, void* stream) {
-  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
-  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
-  if (n_tokens < 0 || vocab < 1 || E < 1)
-    return fail(TP_ERR_INVALID_ARG, "n_tokens = %lld, vocab = %lld, E = %lld: need n_tokens >= 0, vocab > 0, E > 0",
-                (long long)n_tokens, (long long)vocab, (long long)E);
-  if (table_shard == nullptr || (n_tokens > 0 && (tokens == nullptr || out == nullptr)))
-    return fail(TP_ERR_INVALID_ARG, "tokens, table_shard and out must be non-NULL");
-  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
-  if (n_tokens > INT_MAX || vocab > INT_MAX || E > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
-  if (E % 8) return fail(TP_ERR_UNSUPPORTED, "E = %lld must be a multiple of 8", (long long)E);
-  if (!aligned(table_shard, 16) || !aligned(out, 16) || !aligned(tokens, 4))
-    return fail(TP_ERR_UNSUPPORTED, "table_shard and out must be 16-byte aligned, tokens 4-byte aligned");
-  if (n_tokens == 0) return ok();
-  const int64_t rows = width_of(vocab, tp_size, rank);
-  int64_t off = 0;
-  for (int q = 0; q < rank; ++q) off += width_of(vocab, tp_size, q);
-  return hip_status(tpk::launch_embed_shard(tokens, (int)n_tokens, (int)vocab, (int)rows, (int)off,
-                                            static_cast<const uint16_t*>(table_shard), (int)E,
-                                            static_cast<uint16_t*>(out), as_stream(stream)),
-                    "tp_vocab_embedding launch");
-}
-
-TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
-                          const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream) {
+int row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
+                       const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream,
+                       const Tuning& tune) {
   if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
   if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
   if (w_shard == nullptr || (M > 0 && (x_shard == nullptr || y_partial == nullptr)))
@@ -288,11 +241,11 @@ TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logic
   p.ep.act = TP_ACT_NONE;
   p.ep.out_f32 = 1;
   p.ep.accumulate = accumulate;
-  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_row_linear_partial launch");
+  return hip_status(tpk::launch_gemm(p, tune.tile, tune.path, as_stream(stream)), "tp_row_linear_partial launch");
 }
 
-TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv,
-                         int64_t ff, int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream) {
+int qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv, int64_t ff,
+               int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream, const Tuning& tune) {
   HeadDims d;
   int st = resolve_heads(heads, padded_heads, qkv, ff, tp_size, rank, &d);
   if (st != TP_OK) return st;
@@ -328,7 +281,7 @@ TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads,
   g.ep.c_head_w = (int)d.fph;
   g.ep.c_head_pitch = (int)d.fused;
   g.ep.c_head_off = (int)qkv;
-  hipError_t e = tpk::launch_gemm(g, g_tile_override, g_path_override, s);
+  hipError_t e = tpk::launch_gemm(g, tune.tile, tune.path, s);
   if (e != hipSuccess || q == nullptr) return hip_status(e, "tp_qwi_swiglu SwiGLU launch");
   // Query columns: output column c = h * qkv + t reads row h * qph + t, stored densely.
   tpk::GemmProblem a = p;
@@ -338,12 +291,12 @@ TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads,
   a.b_head_off = 0;
   a.ep.C = q;
   a.ep.ldc = d.h_r * qkv;
-  return hip_status(tpk::launch_gemm(a, g_tile_override, g_path_override, s), "tp_qwi_swiglu query launch");
+  return hip_status(tpk::launch_gemm(a, tune.tile, tune.path, s), "tp_qwi_swiglu query launch");
 }
 
-TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
-                           int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
-                           int accumulate, void* stream) {
+int o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv, int64_t ff,
+                 int64_t E, int tp_size, int rank, const void* w_o, float* y_partial, int accumulate, void* stream,
+                 const Tuning& tune) {
   HeadDims d;
   int st = resolve_heads(heads, padded_heads, qkv, ff, tp_size, rank, &d);
   if (st != TP_OK) return st;
@@ -372,7 +325,190 @@ TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_
   p.ep.act = TP_ACT_NONE;
   p.ep.out_f32 = 1;
   p.ep.accumulate = accumulate;
-  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, as_stream(stream)), "tp_o_wo_partial launch");
+  return hip_status(tpk::launch_gemm(p, tune.tile, tune.path, as_stream(stream)), "tp_o_wo_partial launch");
+}
+
+int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
+                          const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                          int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
+                          size_t workspace_bytes, void* stream, const Tuning& tune) {
+  tpk::GemmProblem p;
+  int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, TP_ACT_NONE, y, y_dtype,
+                          layout, ldy, &p);
+  if (st != TP_OK) return st;
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(TP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (scale != nullptr && !aligned(scale, 16)) return fail(TP_ERR_UNSUPPORTED, "scale must be 16-byte aligned");
+  if (xnorm_out != nullptr && !aligned(xnorm_out, 16))
+    return fail(TP_ERR_UNSUPPORTED, "xnorm_out must be 16-byte aligned");
+  if (workspace == nullptr && M > 0) return fail(TP_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t need = tp_rmsnorm_workspace_min_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, at least %zu needed", workspace_bytes, need);
+  if (M == 0) return ok();
+
+  // Workspace: r [M] f32 | t [K] bf16 | (fast path) the normalised rows [M, K] bf16.
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* r = reinterpret_cast<float*>(ws);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws + align_up((size_t)M * 4, 256));
+  uint16_t* rows = xnorm_out != nullptr ? static_cast<uint16_t*>(xnorm_out)
+                   : workspace_bytes >= tp_rmsnorm_workspace_bytes(M, K) ? reinterpret_cast<uint16_t*>(ws + need)
+                                                                         : nullptr;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpk::launch_rmsnorm_rows(static_cast<const uint16_t*>(x), (int)M, (int)K,
+                                          static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr, rows, s);
+  if (e != hipSuccess) return hip_status(e, "rmsnorm statistics launch");
+  if (rows != nullptr) {
+    // Normalised rows materialised: the GEMM reads them as a plain A (direct-to-LDS loop).
+    p.A = rows;
+  } else {
+    // Fused: the GEMM normalises A while staging it (r per row, t per column).
+    p.row_r = r;
+    p.col_t = scale ? t : nullptr;
+  }
+  return hip_status(tpk::launch_gemm(p, tune.tile, tune.path, s), "rmsnorm_column_linear GEMM launch");
+}
+
+int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                         int64_t max_rows_per_chunk, const void* w_shard, int w_dtype, const float* w_block_scale,
+                         float* logits, int32_t* argmax_local, float* max_logit, void* workspace,
+                         size_t workspace_bytes, void* stream, const Tuning& tune) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (x == nullptr || w_shard == nullptr || logits == nullptr || argmax_local == nullptr || workspace == nullptr)
+    return fail(TP_ERR_INVALID_ARG, "x, w_shard, logits, argmax_local and workspace must be non-NULL");
+  if (B < 1 || K < 1 || vocab < 1)
+    return fail(TP_ERR_INVALID_ARG, "B = %lld, K = %lld, vocab = %lld must be positive", (long long)B, (long long)K,
+                (long long)vocab);
+  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
+  if (B > INT_MAX || K > INT_MAX || vocab > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (max_rows_per_chunk < 1)
+    return fail(TP_ERR_SHAPE, "max_rows_per_chunk = %lld must be positive", (long long)max_rows_per_chunk);
+  if (w_dtype != TP_DTYPE_BF16 && w_dtype != TP_DTYPE_FP8_E4M3)
+    return fail(TP_ERR_UNSUPPORTED, "w_dtype %d: the weight must be bf16 or fp8 e4m3", w_dtype);
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (w_dtype == TP_DTYPE_FP8_E4M3) {
+    if (K % 128) return fail(TP_ERR_UNSUPPORTED, "fp8 weights need K (%lld) a multiple of 128", (long long)K);
+    if (w_block_scale == nullptr) return fail(TP_ERR_INVALID_ARG, "fp8 weights need w_block_scale");
+    if (!aligned(w_block_scale, 4)) return fail(TP_ERR_UNSUPPORTED, "w_block_scale misaligned");
+  }
+  if (!aligned(x, 16) || !aligned(w_shard, 16) || !aligned(logits, 4) || !aligned(argmax_local, 4) ||
+      (max_logit != nullptr && !aligned(max_logit, 4)))
+    return fail(TP_ERR_UNSUPPORTED, "x and w_shard must be 16-byte aligned, outputs 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const int64_t V_r = width_of(vocab, tp_size, rank);
+  const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
+  const size_t need = tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
+  if (workspace_bytes < need) return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+
+  tpk::LmHeadProblem p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = w_shard;
+  p.wscale = w_dtype == TP_DTYPE_FP8_E4M3 ? w_block_scale : nullptr;
+  p.w_fp8 = w_dtype == TP_DTYPE_FP8_E4M3;
+  p.B = (int)B;
+  p.K = (int)K;
+  p.V = (int)V_r;
+  p.chunk = (int)chunk;
+  p.logits = logits;
+  p.argmax = argmax_local;
+  p.maxval = max_logit;
+  p.workspace = workspace;
+  return hip_status(tpk::launch_lm_head(p, tune.lm_shape, as_stream(stream)), "lm_head_shard_argmax launch");
+}
+
+}  // namespace tpabi
+
+extern "C" {
+
+TP_API const char* tp_last_error(void) { return g_err; }
+
+TP_API const char* tp_version(void) { return "tpshard 0.1 gfx950"; }
+
+TP_API int tp_shard_widths(const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int64_t* width,
+                    int64_t* logical_off, int64_t* local_off, int64_t* shard_total) {
+  Shard sh;
+  int st = resolve_shard(subparam_sizes, n_sub, tp_size, rank, &sh);
+  if (st != TP_OK) return st;
+  for (int i = 0; i < n_sub; ++i) {
+    if (width) width[i] = sh.width[i];
+    if (logical_off) logical_off[i] = sh.logical_off[i];
+    if (local_off) local_off[i] = sh.local_off[i];
+  }
+  if (shard_total) *shard_total = sh.total;
+  return ok();
+}
+
+TP_API int tp_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                     const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y, int y_dtype,
+                     int layout, int64_t ldy, void* stream) {
+  return tpabi::column_linear(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, act, y, y_dtype,
+                              layout, ldy, stream, tpabi::Tuning{});
+}
+
+TP_API int tp_quantize_rows_e4m3(const void* x, int64_t M, int64_t K, void* q, float* scale, void* stream) {
+  if (M < 0 || K <= 0) return fail(TP_ERR_INVALID_ARG, "M = %lld, K = %lld: need M >= 0, K > 0", (long long)M, (long long)K);
+  if (M > 0 && (x == nullptr || q == nullptr || scale == nullptr))
+    return fail(TP_ERR_INVALID_ARG, "x, q and scale must be non-NULL");
+  if (M > INT_MAX || K > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "M and K must fit in 31 bits");
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4))
+    return fail(TP_ERR_UNSUPPORTED, "x and q must be 16-byte aligned, scale 4-byte aligned");
+  if (M == 0) return ok();
+  return hip_status(tpk::launch_quantize_rows_e4m3(static_cast<const uint16_t*>(x), (int)M, (int)K,
+                                                   static_cast<uint8_t*>(q), scale, as_stream(stream)),
+                    "tp_quantize_rows_e4m3 launch");
+}
+
+TP_API int tp_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
+                                const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
+                                int tp_size, int rank, int act, void* y, int y_dtype, int layout, int64_t ldy,
+                                void* stream) {
+  return tpabi::column_linear_fp8(x_q, x_scale, M, K, w_q, w_scale, bias_shard, subparam_sizes, n_sub, tp_size, rank,
+                                  act, y, y_dtype, layout, ldy, stream, tpabi::Tuning{});
+}
+
+TP_API int tp_vocab_embedding(const int32_t* tokens, int64_t n_tokens, int64_t vocab, int tp_size, int rank,
+                              const void* table_shard, int64_t E, void* out, void* stream) {
+  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
+  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
+  if (n_tokens < 0 || vocab < 1 || E < 1)
+    return fail(TP_ERR_INVALID_ARG, "n_tokens = %lld, vocab = %lld, E = %lld: need n_tokens >= 0, vocab > 0, E > 0",
+                (long long)n_tokens, (long long)vocab, (long long)E);
+  if (table_shard == nullptr || (n_tokens > 0 && (tokens == nullptr || out == nullptr)))
+    return fail(TP_ERR_INVALID_ARG, "tokens, table_shard and out must be non-NULL");
+  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
+  if (n_tokens > INT_MAX || vocab > INT_MAX || E > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (E % 8) return fail(TP_ERR_UNSUPPORTED, "E = %lld must be a multiple of 8", (long long)E);
+  if (!aligned(table_shard, 16) || !aligned(out, 16) || !aligned(tokens, 4))
+    return fail(TP_ERR_UNSUPPORTED, "table_shard and out must be 16-byte aligned, tokens 4-byte aligned");
+  if (n_tokens == 0) return ok();
+  const int64_t rows = width_of(vocab, tp_size, rank);
+  int64_t off = 0;
+  for (int q = 0; q < rank; ++q) off += width_of(vocab, tp_size, q);
+  return hip_status(tpk::launch_embed_shard(tokens, (int)n_tokens, (int)vocab, (int)rows, (int)off,
+                                            static_cast<const uint16_t*>(table_shard), (int)E,
+                                            static_cast<uint16_t*>(out), as_stream(stream)),
+                    "tp_vocab_embedding launch");
+}
+
+TP_API int tp_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
+                          const void* bias, int tp_size, int rank, float* y_partial, int accumulate, void* stream) {
+  return tpabi::row_linear_partial(x_shard, M, K_logical, N, w_shard, bias, tp_size, rank, y_partial, accumulate,
+                                   stream, tpabi::Tuning{});
+}
+
+TP_API int tp_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv,
+                         int64_t ff, int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream) {
+  return tpabi::qwi_swiglu(xnorm, M, E, heads, padded_heads, qkv, ff, tp_size, rank, w_qwi, q, y_fused, stream,
+                           tpabi::Tuning{});
+}
+
+TP_API int tp_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
+                           int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
+                           int accumulate, void* stream) {
+  return tpabi::o_wo_partial(y_fused, M, heads, padded_heads, qkv, ff, E, tp_size, rank, w_o, y_partial, accumulate,
+                             stream, tpabi::Tuning{});
 }
 
 TP_API int tp_reduce_scatter_residual(const float* const* partials, int tp_size, int64_t batch, int64_t seq,
@@ -430,41 +566,9 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
                                  const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
                                  int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  tpk::GemmProblem p;
-  int st = prepare_column(x, M, K, w_shard, bias_shard, subparam_sizes, n_sub, tp_size, rank, TP_ACT_NONE, y, y_dtype,
-                          layout, ldy, &p);
-  if (st != TP_OK) return st;
-  if (!(eps >= 0.0f) || isinf(eps)) return fail(TP_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  if (scale != nullptr && !aligned(scale, 16)) return fail(TP_ERR_UNSUPPORTED, "scale must be 16-byte aligned");
-  if (xnorm_out != nullptr && !aligned(xnorm_out, 16))
-    return fail(TP_ERR_UNSUPPORTED, "xnorm_out must be 16-byte aligned");
-  if (workspace == nullptr && M > 0) return fail(TP_ERR_INVALID_ARG, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const size_t need = tp_rmsnorm_workspace_min_bytes(M, K);
-  if (workspace_bytes < need)
-    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, at least %zu needed", workspace_bytes, need);
-  if (M == 0) return ok();
-
-  // Workspace: r [M] f32 | t [K] bf16 | (fast path) the normalised rows [M, K] bf16.
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* r = reinterpret_cast<float*>(ws);
-  uint16_t* t = reinterpret_cast<uint16_t*>(ws + align_up((size_t)M * 4, 256));
-  uint16_t* rows = xnorm_out != nullptr ? static_cast<uint16_t*>(xnorm_out)
-                   : workspace_bytes >= tp_rmsnorm_workspace_bytes(M, K) ? reinterpret_cast<uint16_t*>(ws + need)
-                                                                         : nullptr;
-  hipStream_t s = as_stream(stream);
-  hipError_t e = tpk::launch_rmsnorm_rows(static_cast<const uint16_t*>(x), (int)M, (int)K,
-                                          static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr, rows, s);
-  if (e != hipSuccess) return hip_status(e, "rmsnorm statistics launch");
-  if (rows != nullptr) {
-    // Normalised rows materialised: the GEMM reads them as a plain A (direct-to-LDS loop).
-    p.A = rows;
-  } else {
-    // Fused: the GEMM normalises A while staging it (r per row, t per column).
-    p.row_r = r;
-    p.col_t = scale ? t : nullptr;
-  }
-  return hip_status(tpk::launch_gemm(p, g_tile_override, g_path_override, s), "rmsnorm_column_linear GEMM launch");
+  return tpabi::rmsnorm_column_linear(x, M, K, scale, eps, xnorm_out, w_shard, bias_shard, subparam_sizes, n_sub,
+                                      tp_size, rank, y, y_dtype, layout, ldy, workspace, workspace_bytes, stream,
+                                      tpabi::Tuning{});
 }
 
 TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk) {
@@ -480,71 +584,9 @@ TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t voc
                          int64_t max_rows_per_chunk, const void* w_shard, int w_dtype, const float* w_block_scale,
                          float* logits, int32_t* argmax_local, float* max_logit, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  if (tp_size < 1) return fail(TP_ERR_INVALID_ARG, "tp_size = %d must be >= 1", tp_size);
-  if (rank < 0 || rank >= tp_size) return fail(TP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, tp_size);
-  if (x == nullptr || w_shard == nullptr || logits == nullptr || argmax_local == nullptr || workspace == nullptr)
-    return fail(TP_ERR_INVALID_ARG, "x, w_shard, logits, argmax_local and workspace must be non-NULL");
-  if (B < 1 || K < 1 || vocab < 1)
-    return fail(TP_ERR_INVALID_ARG, "B = %lld, K = %lld, vocab = %lld must be positive", (long long)B, (long long)K,
-                (long long)vocab);
-  if (vocab < tp_size) return fail(TP_ERR_SHAPE, "vocab %lld is smaller than tp_size %d", (long long)vocab, tp_size);
-  if (B > INT_MAX || K > INT_MAX || vocab > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
-  if (max_rows_per_chunk < 1)
-    return fail(TP_ERR_SHAPE, "max_rows_per_chunk = %lld must be positive", (long long)max_rows_per_chunk);
-  if (w_dtype != TP_DTYPE_BF16 && w_dtype != TP_DTYPE_FP8_E4M3)
-    return fail(TP_ERR_UNSUPPORTED, "w_dtype %d: the weight must be bf16 or fp8 e4m3", w_dtype);
-  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
-  if (w_dtype == TP_DTYPE_FP8_E4M3) {
-    if (K % 128) return fail(TP_ERR_UNSUPPORTED, "fp8 weights need K (%lld) a multiple of 128", (long long)K);
-    if (w_block_scale == nullptr) return fail(TP_ERR_INVALID_ARG, "fp8 weights need w_block_scale");
-    if (!aligned(w_block_scale, 4)) return fail(TP_ERR_UNSUPPORTED, "w_block_scale misaligned");
-  }
-  if (!aligned(x, 16) || !aligned(w_shard, 16) || !aligned(logits, 4) || !aligned(argmax_local, 4) ||
-      (max_logit != nullptr && !aligned(max_logit, 4)))
-    return fail(TP_ERR_UNSUPPORTED, "x and w_shard must be 16-byte aligned, outputs 4-byte aligned");
-  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const int64_t V_r = width_of(vocab, tp_size, rank);
-  const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
-  const size_t need = tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
-  if (workspace_bytes < need) return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-
-  tpk::LmHeadProblem p;
-  p.x = static_cast<const uint16_t*>(x);
-  p.w = w_shard;
-  p.wscale = w_dtype == TP_DTYPE_FP8_E4M3 ? w_block_scale : nullptr;
-  p.w_fp8 = w_dtype == TP_DTYPE_FP8_E4M3;
-  p.B = (int)B;
-  p.K = (int)K;
-  p.V = (int)V_r;
-  p.chunk = (int)chunk;
-  p.logits = logits;
-  p.argmax = argmax_local;
-  p.maxval = max_logit;
-  p.workspace = workspace;
-  return hip_status(tpk::launch_lm_head(p, g_lm_shape_override, as_stream(stream)), "lm_head_shard_argmax launch");
-}
-
-TP_API int tp_debug_set_gemm_tile(int tile) {
-  if (tile < tpk::TILE_AUTO || tile >= tpk::TILE_COUNT) return fail(TP_ERR_INVALID_ARG, "unknown tile %d", tile);
-  g_tile_override = tile;
-  return ok();
-}
-
-TP_API int tp_debug_set_gemm_path(int path) {
-  if (path < tpk::GEMM_PATH_AUTO || path > tpk::GEMM_PATH_DMA) return fail(TP_ERR_INVALID_ARG, "unknown path %d", path);
-  g_path_override = path;
-  return ok();
-}
-
-TP_API int tp_debug_set_lm_head_shape(int shape) {
-  if (shape < -1 || shape >= tpk::lm_head_shape_count()) return fail(TP_ERR_INVALID_ARG, "unknown shape %d", shape);
-  g_lm_shape_override = shape;
-  return ok();
-}
-
-TP_API int tp_debug_gemm_pick_tile(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 1 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return -1;
-  return tpk::gemm_pick_tile((int)M, (int)N, (int)K);
+  return tpabi::lm_head_shard_argmax(x, B, K, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w_dtype, w_block_scale,
+                                     logits, argmax_local, max_logit, workspace, workspace_bytes, stream,
+                                     tpabi::Tuning{});
 }
 
 }  // extern "C"

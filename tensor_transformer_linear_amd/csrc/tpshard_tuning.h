@@ -1,0 +1,63 @@
+/*
+ * tpshard_tuning.h - launch-choice variants of libtpshard's entry points, exported by the
+ * separate tuning library libtpshard_tuning.so (tests and measurements only; the product
+ * library libtpshard.so exports none of these and keeps no state that selects kernels).
+ *
+ * Each tpt_X takes the arguments of tp_X / X in tpshard.h, in the same order, followed by
+ * the launch choices:
+ *   tile      -1: automatic; 0..6 force the GEMM tile 256x256, 256x128, 128x128, 128x256,
+ *             256x224, 128x64, 64x64 (output rows x columns per workgroup). The fp8 GEMM
+ *             takes 0 or 2 and treats any other value as automatic.
+ *   path      -1: automatic; 0: register-staged operands; 1: direct-to-LDS loads (needs
+ *             K % 32 == 0 and no RMSNorm transform; a call that cannot use it returns
+ *             TP_ERR_HIP).
+ *   lm_shape  -1: the default LM-head kernel; otherwise an index into the LM head's launch
+ *             shapes (tpt_lm_head_shape_count() of them).
+ * An unknown choice returns TP_ERR_INVALID_ARG before any check of the other arguments.
+ * Error messages are read with this library's own tp_last_error().
+ */
+#ifndef TPSHARD_TUNING_H
+#define TPSHARD_TUNING_H
+
+#include "tpshard.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+TP_API int tpt_column_linear(const void* x, int64_t M, int64_t K, const void* w_shard, const void* bias_shard,
+                             const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, int act, void* y,
+                             int y_dtype, int layout, int64_t ldy, void* stream, int tile, int path);
+TP_API int tpt_column_linear_fp8(const void* x_q, const float* x_scale, int64_t M, int64_t K, const void* w_q,
+                                 const float* w_scale, const void* bias_shard, const int64_t* subparam_sizes,
+                                 int n_sub, int tp_size, int rank, int act, void* y, int y_dtype, int layout,
+                                 int64_t ldy, void* stream, int tile);
+TP_API int tpt_row_linear_partial(const void* x_shard, int64_t M, int64_t K_logical, int64_t N, const void* w_shard,
+                                  const void* bias, int tp_size, int rank, float* y_partial, int accumulate,
+                                  void* stream, int tile, int path);
+TP_API int tpt_qwi_swiglu(const void* xnorm, int64_t M, int64_t E, int64_t heads, int64_t padded_heads, int64_t qkv,
+                          int64_t ff, int tp_size, int rank, const void* w_qwi, void* q, void* y_fused, void* stream,
+                          int tile, int path);
+TP_API int tpt_o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_heads, int64_t qkv,
+                            int64_t ff, int64_t E, int tp_size, int rank, const void* w_o, float* y_partial,
+                            int accumulate, void* stream, int tile, int path);
+TP_API int tpt_rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps,
+                                     void* xnorm_out, const void* w_shard, const void* bias_shard,
+                                     const int64_t* subparam_sizes, int n_sub, int tp_size, int rank, void* y,
+                                     int y_dtype, int layout, int64_t ldy, void* workspace, size_t workspace_bytes,
+                                     void* stream, int tile, int path);
+TP_API int tpt_lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                                    int64_t max_rows_per_chunk, const void* w_shard, int w_dtype,
+                                    const float* w_block_scale, float* logits, int32_t* argmax_local,
+                                    float* max_logit, void* workspace, size_t workspace_bytes, void* stream,
+                                    int lm_shape);
+/* The automatic tile for an M x N x K bf16 GEMM (-1 for invalid sizes), and the number of
+ * LM-head launch shapes. */
+TP_API int tpt_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
+TP_API int tpt_lm_head_shape_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_TUNING_H */

@@ -30,19 +30,42 @@ WS = ctypes.c_void_p(0x40000)      # 256-byte aligned
 MIS = ctypes.c_void_p(0x10002)     # misaligned
 
 
-def declared_functions():
-    text = open(HEADER).read()
+TUNING_HEADER = os.path.join(ROOT, "tensor_transformer_linear_amd", "csrc", "tpshard_tuning.h")
+
+
+def declared_functions(path=HEADER):
+    text = open(path).read()
     return set(re.findall(r"^TP_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M))
+
+
+def exported_functions(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
 
 
 def test_exports_match_header():
     declared = declared_functions()
     assert {"tp_shard_widths", "tp_column_linear", "tp_row_linear_partial", "rmsnorm_column_linear",
             "lm_head_shard_argmax"} <= declared
-    out = subprocess.run(["nm", "-D", "--defined-only", tt.LIB_PATH], capture_output=True, text=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
-    assert exported == declared
+    assert exported_functions(tt.LIB_PATH) == declared
     assert declared == set(tt.SIGNATURES)
+
+
+def test_public_header_has_no_launch_switch():
+    """The product ABI holds no call that selects kernels, and the library keeps no state for it:
+    the launch-choice variants live in the separate tuning library only."""
+    text = open(HEADER).read()
+    for word in ("tp_debug", "tpt_", "set_gemm", "lm_head_shape"):
+        assert word not in text, word
+    src = open(os.path.join(ROOT, "tensor_transformer_linear_amd", "csrc", "tpshard_abi.hip")).read()
+    assert src.count("thread_local") == 1 and "thread_local char g_err" in src
+
+
+def test_tuning_library_exports():
+    tuned = declared_functions(TUNING_HEADER)
+    assert tuned and all(n.startswith("tpt_") for n in tuned)
+    assert exported_functions(tt.TUNING_LIB_PATH) == declared_functions() | tuned
+    assert tuned == {n for n in tt.TUNING_SIGNATURES if n.startswith("tpt_")}
 
 
 def test_version():
@@ -178,13 +201,35 @@ def test_lm_head_workspace_query():
     assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0, 0) == 0
 
 
-def test_debug_tile_hook():
-    with pytest.raises(tt.TpError):
-        tt.set_gemm_tile(99)
-    tt.set_gemm_tile(3)
-    tt.set_gemm_tile(-1)
+def test_tuning_choices_checked_before_anything_else():
+    T = tt.tuning_lib()
+    sizes = _sizes([64])
+    for tile, path in ((99, -1), (-2, -1), (0, 5), (0, -2)):
+        assert T.tpt_column_linear(A, 64, 128, A2, None, sizes, 1, 1, 0, 0, A3, 0, 0, 64, None, tile, path) == \
+            tt.TP_ERR_INVALID_ARG
+        assert b"unknown" in T.tp_last_error()
+    n = T.tpt_lm_head_shape_count()
+    assert n == len(tt.LM_HEAD_SHAPES)
+    assert T.tpt_lm_head_shard_argmax(A, 32, 256, 4096, 8, 0, 512, A2, 0, None, A3, A, A2, WS, 1 << 20, None, n) == \
+        tt.TP_ERR_INVALID_ARG
     assert tt.gemm_pick_tile(0, 1, 1) == -1
     assert tt.gemm_pick_tile(32768, 3072, 8192) in tt.GEMM_TILES
+
+
+def test_tuning_routing_restores_the_product_library():
+    assert getattr(tt._tls, "choices", None) is None
+    with tt.tuning(tile=3):
+        assert tt._tls.choices == {"tile": 3, "path": -1, "lm_shape": -1}
+        with tt.tuning(lm_shape=9):
+            assert tt._tls.choices["lm_shape"] == 9 and tt._tls.choices["tile"] == -1
+        assert tt._tls.choices["tile"] == 3
+    assert tt._tls.choices is None
+    tt.set_gemm_tile(2)
+    tt.set_gemm_path(1)
+    tt.set_gemm_tile(-1)
+    assert tt._tls.choices == {"tile": -1, "path": 1, "lm_shape": -1}
+    tt.set_gemm_path(-1)
+    assert tt._tls.choices is None
 
 
 def test_product_path_does_not_use_the_oracle_or_generator():
