@@ -49,6 +49,9 @@ def parse():
                     help="1: also time the legs beyond the five workloads: the fp8 prefill column linear, the "
                          "fused q_wi + SwiGLU and o_wo projections, the embedding and the sequence-parallel "
                          "reduce-scatter with residual (0 = skip)")
+    ap.add_argument("--gemm-launches", type=int, default=0, metavar="N",
+                    help="only launch each GEMM of the hot path N times in a fixed order (workloads 1-4, the fp8 "
+                         "prefill GEMM, q_wi + SwiGLU and o_wo), for per-kernel profiler counters, and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
@@ -192,10 +195,23 @@ class Workloads:
         return s
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(budget_s: float):
-    """The oracle, as it stands, on 256-row blocks of the RMSNorm -> column workload (its
-    32768 rows, cycled) until the time budget is spent; returns TFLOP/s of the GEMM flops it
-    covered."""
+    """The oracle, as it stands, on each workload of a step: workloads 1-3 and both LM heads
+    in full, workload 4 on 256-row blocks of its 32768 rows (cycled) for the oracle time the
+    others leave of ``budget_s`` (input generation is not timed). Returns the headline (the
+    GEMM TFLOP/s of workloads 1-4, workload 4 scaled from its sample) with one entry per
+    workload."""
     import oracle
     import synth
 
@@ -205,26 +221,85 @@ def cpu_baseline(budget_s: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    c = synth.WORKLOADS[4]
-    rows_per_block = 256
+    W = synth.WORKLOADS
+    per = []
+    t_all = time.perf_counter()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # workload 1: both ranks of the GPT-2 MLP shard and their rank-ordered sum
+    c = W[1]
+    inp = synth.workload_inputs(1)
+    shards = [(oracle.take_column_shard(inp["w_fc"], [c["inter"]], c["tp"], r),
+               oracle.take_row_shard(inp["w_proj"], c["tp"], r)) for r in range(c["tp"])]
+
+    def wl1():
+        parts = [oracle.mlp_rank(inp["x"], a, b, rank=r)[1] for r, (a, b) in enumerate(shards)]
+        oracle.rank_ordered_sum(parts)
+    m = inp["x"].shape[0]
+    per.append((1, 2.0 * m * c["inter"] // c["tp"] * c["hidden"] * 2 * c["tp"], timed(wl1), "both ranks, full"))
+    # workload 2: the fused-QKV column shard with bias
+    c = W[2]
+    inp = synth.workload_inputs(2)
+    rows = oracle.shard_rows(list(c["sizes"]), c["tp"], c["rank"])
+    w2, b2 = np.ascontiguousarray(inp["w"][rows]), np.ascontiguousarray(inp["bias"][rows])
+    per.append((2, 2.0 * inp["x"].shape[0] * len(rows) * c["hidden"],
+                timed(lambda: oracle.column_linear(inp["x"], w2, b2, list(c["sizes"]), c["tp"], c["rank"])), "full"))
+    # workload 3: the Llama-8B MLP shard
+    c = W[3]
+    inp = synth.workload_inputs(3)
+    per.append((3, 2.0 * inp["x"].shape[0] * inp["w_fc"].shape[0] * c["hidden"] * 2,
+                timed(lambda: oracle.mlp_rank(inp["x"], inp["w_fc"], inp["w_proj"], rank=c["rank"])), "full"))
+    # workload 5: the LM head, bf16 and E4M3 weights (GB/s over the bytes the method moves)
+    c = W[5]
+    inp = synth.workload_inputs(5)
+    B, K = inp["x"].shape
+    V = inp["w"].shape[0]
+    lm = []
+    for dt, nbytes, fn in (
+            ("bf16", V * K * 2 + B * K * 2 + B * V * 4,
+             lambda: oracle.shard_argmax(oracle.lm_head_logits(inp["x"], inp["w"], max_rows_per_chunk=c["chunk"]))),
+            ("fp8", V * K + V * (K // 128) * 4 + B * K * 2 + B * V * 4,
+             lambda: oracle.shard_argmax(oracle.lm_head_logits(inp["x"], w_fp8=inp["w_fp8"], w_scale=inp["w_scale"],
+                                                               max_rows_per_chunk=c["chunk"])))):
+        dt_s = timed(fn)
+        lm.append({"workload": 5, "weights": dt, "seconds": round(dt_s, 3), "gbs": round(nbytes / dt_s / 1e9, 2),
+                   "sample": "full"})
+    # workload 4: RMSNorm -> column shard, 256-row blocks for the remaining budget (at least 4 blocks)
+    c = W[4]
     inp = synth.workload_inputs(4)
     x, s, w = inp["x"], inp["scale"], inp["w"]
+    rows_per_block = 256
     n_blocks = x.shape[0] // rows_per_block
+    left = max(1.0, budget_s - sum(t for _, _, t, _ in per) - sum(e["seconds"] for e in lm))
     done = 0
     t0 = time.perf_counter()
-    while True:
+    while done < 4 or time.perf_counter() - t0 < left:
         r0 = (done % n_blocks) * rows_per_block
         oracle.rmsnorm_column_linear(x[r0:r0 + rows_per_block], s, w, None, [c["out_logical"]], c["tp"], c["rank"])
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    rows = done * rows_per_block
-    flops = 2.0 * rows * w.shape[0] * c["hidden"]
+    dt4 = time.perf_counter() - t0
+    rows4 = done * rows_per_block
+    fl4 = 2.0 * rows4 * w.shape[0] * c["hidden"]
+    full4 = 2.0 * x.shape[0] * w.shape[0] * c["hidden"]
+    per.append((4, fl4, dt4, f"{rows4} of the 32768 rows in 256-row blocks"))
+    per.sort()
+    entries = [{"workload": k, "gflop": round(fl / 1e9, 3), "seconds": round(t, 3),
+                "tflops": round(fl / t / 1e12, 4), "sample": smp} for k, fl, t, smp in per]
+    # the headline: the step's GEMM flops over the oracle's time for them, workload 4 scaled to its 32768 rows
+    step_s = sum(t for k, fl, t, _ in per if k != 4) + dt4 * full4 / fl4
+    step_fl = sum(fl for k, fl, t, _ in per if k != 4) + full4
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"RMSNorm -> column shard [3072, 8192]: {rows} rows of the 32768-row workload in 256-row blocks "
-                  f"({dt:.1f} s, numpy float64, {os.cpu_count()} host cpus, {platform.processor() or platform.machine()})",
+        "value": step_fl / step_s / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"numpy float64 oracle on workloads 1-3 in full and {rows4} rows of workload 4 "
+                  f"(the step's GEMM flops over its time, workload 4 scaled to 32768 rows: {step_s:.1f} s per step); "
+                  f"{sum(t for _, _, t, _ in per) + sum(e['seconds'] for e in lm):.1f} s of oracle time "
+                  f"({time.perf_counter() - t_all:.1f} s with input generation); {os.cpu_count()} host cpus, "
+                  f"{_cpu_model()}",
+        "per_config": entries + lm,
     }
 
 
@@ -489,6 +564,65 @@ def embedding_leg(launches, stream):
             "timing": "per-launch HIP events; throughput from the median"}
 
 
+def gemm_launches(n: int) -> None:
+    """Each GEMM launch of the hot path, n times in a row, in a fixed order (a profiler's dispatch
+    list then reads in that order); the labels go to stderr."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    dev = torch.device("cuda:0")
+    wl = Workloads({1, 2, 3, 4}, dev)
+    c4 = wl.c4
+    xn = torch.empty_like(wl.x4)
+    tt.rmsnorm_column_linear(wl.x4, wl.s4, c4["eps"], wl.w4, None, [c4["out_logical"]], c4["tp"], c4["rank"], y=wl.y4,
+                             workspace=wl.ws4, xnorm_out=xn)
+    c1 = wl.c1
+    segs = [
+        ("workload 1 c_fc + GELU, both ranks [256 x 768] x [1536 x 768]^T",
+         lambda: [tt.tp_column_linear(wl.x1, wl.wfc1[r], None, [c1["inter"]], c1["tp"], r, act=tt.TP_ACT_GELU_ERF,
+                                      y=wl.g1[r]) for r in range(2)]),
+        ("workload 1 c_proj partials, both ranks [256 x 1536] x [768 x 1536]^T",
+         lambda: [tt.tp_row_linear_partial(wl.g1[r], c1["inter"], wl.wpj1[r], None, c1["tp"], r, y_partial=wl.s1,
+                                           accumulate=int(r > 0)) for r in range(2)]),
+        ("workload 2 fused QKV [4096 x 4096] x [768 x 4096]^T + bias", wl.part2),
+        ("workload 3 c_fc + GELU [8192 x 4096] x [1792 x 4096]^T", wl.part3a),
+        ("workload 3 c_proj partial [8192 x 1792] x [4096 x 1792]^T", wl.part3b),
+        ("workload 4 column GEMM [32768 x 8192] x [3072 x 8192]^T",
+         lambda: tt.tp_column_linear(xn, wl.w4, None, [c4["out_logical"]], c4["tp"], c4["rank"], y=wl.y4)),
+    ]
+    inp = synth.workload_inputs(4)
+    wq, ws = synth.quantize_e4m3_channels(inp["w"])
+    wq_d, ws_d = torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev)
+    q, sc = tt.tp_quantize_rows_e4m3(wl.x4)
+    segs.append(("fp8 prefill GEMM [32768 x 8192] x [3072 x 8192]^T (E4M3)",
+                 lambda: tt.tp_column_linear_fp8(q, sc, wq_d, ws_d, None, [c4["out_logical"]], c4["tp"], c4["rank"],
+                                                 y=wl.y4)))
+    M, E, heads, qkv, ff, tp = 8192, 8192, 64, 128, 32768, 8
+    h_r, fph = heads // tp, ff // heads
+
+    def normal(shape, std, tid):
+        return torch.from_numpy(synth.bf16_normal(shape, std, 12, tid).view(np.int16)).view(torch.bfloat16).to(dev)
+    xq = normal((M, E), 1.0, 0)
+    wqwi = normal((h_r * (qkv + 2 * fph), E), 0.02, 1)
+    w_o = normal((E, h_r * (qkv + fph)), 0.02, 2)
+    yf = normal((M, h_r, qkv + fph), 1.0, 3)
+    qq = torch.empty((M, h_r, qkv), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, E), dtype=torch.float32, device=dev)
+    segs.append(("q_wi: SwiGLU columns then query columns, E 8192, 8 heads x (128 + 2 x 512)",
+                 lambda: tt.tp_qwi_swiglu(xq, heads, 0, qkv, ff, tp, 0, wqwi, yf, q=qq)))
+    segs.append(("o_wo partial [8192 x 5120] x [8192 x 5120]^T",
+                 lambda: tt.tp_o_wo_partial(yf.view(M, -1), heads, 0, qkv, ff, tp, 0, w_o, out)))
+    torch.cuda.synchronize()
+    for label, fn in segs:
+        print(f"gemm-launches: {n} x {label}", file=sys.stderr, flush=True)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+    print(json.dumps({"gemm_launches": n, "segments": [l for l, _ in segs]}), flush=True)
+
+
 def copy_probe(mb: int):
     """Plain device-to-device copies of a known size: the reference for HBM byte counters."""
     import torch
@@ -516,6 +650,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe > 0:
         copy_probe(args.copy_probe)
+        return
+    if args.gemm_launches > 0:
+        gemm_launches(args.gemm_launches)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

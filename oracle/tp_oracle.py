@@ -190,6 +190,26 @@ def gelu_erf(a32: np.ndarray) -> np.ndarray:
     return 0.5 * a * _erfc(-a / math.sqrt(2.0))
 
 
+def linear_sums(x_bits, w_bits, bias_bits=None) -> np.ndarray:
+    """The exact sums ``sum_k x[m,k] W[j,k] (+ b[j])`` in float64, before any rounding.
+
+    [deepspeed] ``forward``: ``input @ weight.T`` then ``+ bias``.  Every product of two bf16
+    values is exact in float64.  The linear layers below round these sums; the tests use them
+    to check that a GPU output one bf16 unit away from the oracle's is a rounding straddle.
+    """
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x and weight K differ")
+    acc = x @ w.T
+    if bias_bits is not None:
+        b = bf16_to_f64(bias_bits)
+        if b.shape != (w.shape[0],):
+            raise ValueError(f"bias has {b.size} entries, expected {w.shape[0]}")
+        acc = acc + b[None, :]
+    return acc
+
+
 def column_linear(x_bits, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size, rank,
                   act=ACT_NONE, out_dtype=OUT_BF16, layout=LAYOUT_LOCAL, n_logical=None):
     """One rank's column-parallel linear with sub-parameter sharding.
@@ -210,20 +230,10 @@ def column_linear(x_bits, w_shard_bits, bias_shard_bits, subparam_sizes, tp_size
     rank's columns placed at their logical positions in ``[M, n_logical]`` and a
     boolean mask of the columns this rank wrote (the others are untouched).
     """
-    x = bf16_to_f64(x_bits)
-    w = bf16_to_f64(w_shard_bits)
     width, loff, lcl, total = shard_widths(subparam_sizes, tp_size, rank)
-    if w.shape[0] != total:
-        raise ValueError(f"weight shard has {w.shape[0]} rows, shard total is {total}")
-    if x.shape[1] != w.shape[1]:
-        raise ValueError("x and weight K differ")
-    acc = x @ w.T
-    if bias_shard_bits is not None:
-        b = bf16_to_f64(bias_shard_bits)
-        if b.shape != (total,):
-            raise ValueError(f"bias shard has {b.size} entries, expected {total}")
-        acc = acc + b[None, :]
-    a = f32(acc)
+    if np.shape(w_shard_bits)[0] != total:
+        raise ValueError(f"weight shard has {np.shape(w_shard_bits)[0]} rows, shard total is {total}")
+    a = f32(linear_sums(x_bits, w_shard_bits, bias_shard_bits))
     if act == ACT_GELU:
         a = f32(gelu_erf(a))
     y = bf16_round(a) if out_dtype == OUT_BF16 else a
@@ -292,7 +302,15 @@ def mlp_rank(x_bits, w_fc_shard_bits, w_proj_shard_bits, rank=0, y_prev=None):
 # O5 - RMSNorm prologue  [palm] allgather_layernorm, transformer_layer_weight_gathered
 # --------------------------------------------------------------------------------------
 
-def rmsnorm(x_bits, scale_bits=None, eps=RMS_EPS):
+def rmsnorm_factor(x_bits, eps=RMS_EPS) -> np.ndarray:
+    """The exact per-row factor ``1 / sqrt(mean_k x^2 + eps)`` in float64 (before its float32
+    rounding): [palm] ``allgather_layernorm``'s ``rsqrt(mean2 + eps)`` over the whole row."""
+    x = bf16_to_f64(x_bits)
+    ms = np.sum(x * x, axis=1) / x.shape[1]
+    return 1.0 / np.sqrt(ms + eps)
+
+
+def rmsnorm(x_bits, scale_bits=None, eps=RMS_EPS, r=None):
     """bf16 RMS-normalised rows, as the [palm] layer computes them before ``q_wi``.
 
     Per row: mean of squares in (at least) float32 over the whole hidden
@@ -301,12 +319,12 @@ def rmsnorm(x_bits, scale_bits=None, eps=RMS_EPS):
     With a learned scale the page adds 1 to the bf16 scale first, so
     ``t = bf16(f32(1 + s))`` and ``y = bf16(n * t)`` (the product of two bf16
     values is exact in float32).  Without a scale (the prefill layer's local
-    norm) ``y = n``.  Returns ``(y_bits uint16 [M, K], r float32 [M])``.
+    norm) ``y = n``.  ``r`` (float32 ``[M]``), when given, replaces the computed
+    factor: the rows another admissible float32 rounding of the factor gives.
+    Returns ``(y_bits uint16 [M, K], r float32 [M])``.
     """
     x = bf16_to_f64(x_bits)
-    k = x.shape[1]
-    ms = np.sum(x * x, axis=1) / k
-    r = f32(1.0 / np.sqrt(ms + eps))
+    r = f32(rmsnorm_factor(x_bits, eps)) if r is None else np.asarray(r, dtype=np.float32)
     n = bf16_round(f32(x * r.astype(np.float64)[:, None]))
     if scale_bits is None:
         return n, r
@@ -352,18 +370,17 @@ def vocab_shard(vocab: int, tp_size: int, rank: int):
     return width[0], loff[0]
 
 
-def lm_head_logits(x_bits, w_shard_bits=None, w_fp8=None, w_scale=None, max_rows_per_chunk=None):
-    """float32 logits of one vocab shard, chunk by chunk, concatenated.
+def lm_head_sums(x_bits, w_shard_bits=None, w_fp8=None, w_scale=None, max_rows_per_chunk=None):
+    """float64 logits of one vocab shard before their float32 rounding, chunk by chunk,
+    concatenated.
 
     [tt] ``LMHead1D.forward``: one linear per weight split, outputs trimmed to
     their logical widths and concatenated along the vocab dimension; each device
     ends with the complete logits of its vocab shard (no partial sums).
-    [palm] ``unembed_manual`` computes logits in float32.
 
-    bf16 weight: ``logits[b,v] = f32(sum_k x[b,k] W[v,k])``.
-    E4M3 weight with per-row, per-128-K block scales (reading of the page's
-    8-bit block weight format):
-    ``logits[b,v] = f32(sum_blk s[v,blk] * sum_{k in blk} x[b,k] dec(q[v,k]))``.
+    bf16 weight: ``sum_k x[b,k] W[v,k]``.  E4M3 weight with per-row, per-128-K
+    block scales (reading of the page's 8-bit block weight format):
+    ``sum_blk s[v,blk] * sum_{k in blk} x[b,k] dec(q[v,k])``.
     """
     x = bf16_to_f64(x_bits)
     if w_shard_bits is not None:
@@ -388,8 +405,13 @@ def lm_head_logits(x_bits, w_shard_bits=None, w_fp8=None, w_scale=None, max_rows
             return part
     c = v_rows if max_rows_per_chunk is None else max_rows_per_chunk
     sizes, offs = lm_head_chunks(v_rows, c)
-    outs = [chunk(o, o + n) for n, o in zip(sizes, offs)]
-    return f32(np.concatenate(outs, axis=1))
+    return np.concatenate([chunk(o, o + n) for n, o in zip(sizes, offs)], axis=1)
+
+
+def lm_head_logits(x_bits, w_shard_bits=None, w_fp8=None, w_scale=None, max_rows_per_chunk=None):
+    """float32 logits of one vocab shard: ``f32`` of ``lm_head_sums`` ([palm]
+    ``unembed_manual`` computes logits in float32)."""
+    return f32(lm_head_sums(x_bits, w_shard_bits, w_fp8, w_scale, max_rows_per_chunk))
 
 
 def shard_argmax(logits32: np.ndarray):
@@ -479,6 +501,22 @@ def quantize_rows_e4m3(x_bits):
     return q, s
 
 
+def linear_sums_fp8(xq, x_scale, wq, w_scale, bias_bits=None) -> np.ndarray:
+    """``x_scale[m] * w_scale[j] * sum_k dec(xq[m,k]) dec(wq[j,k]) (+ b[j])`` in float64, before
+    any rounding (every product of two E4M3 values is exact)."""
+    x = e4m3_to_f64(xq)
+    w = e4m3_to_f64(wq)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("x and weight K differ")
+    v = np.asarray(x_scale, np.float64)[:, None] * np.asarray(w_scale, np.float64)[None, :] * (x @ w.T)
+    if bias_bits is not None:
+        b = bf16_to_f64(bias_bits)
+        if b.shape != (w.shape[0],):
+            raise ValueError(f"bias has {b.size} entries, expected {w.shape[0]}")
+        v = v + b[None, :]
+    return v
+
+
 def column_linear_fp8(xq, x_scale, wq_shard, w_scale_shard, bias_shard_bits, subparam_sizes, tp_size, rank,
                       act=ACT_NONE, out_dtype=OUT_BF16, layout=LAYOUT_LOCAL, n_logical=None):
     """One rank's column-parallel linear on E4M3 activations and weights.
@@ -488,21 +526,10 @@ def column_linear_fp8(xq, x_scale, wq_shard, w_scale_shard, bias_shard_bits, sub
     ``column_linear``: ``a = f32(v)``, GELU on ``a`` if asked, one rounding to the output
     type, LOCAL or LOGICAL placement of the shard's columns.
     """
-    x = e4m3_to_f64(xq)
-    w = e4m3_to_f64(wq_shard)
     width, loff, lcl, total = shard_widths(subparam_sizes, tp_size, rank)
-    if w.shape[0] != total:
-        raise ValueError(f"weight shard has {w.shape[0]} rows, shard total is {total}")
-    if x.shape[1] != w.shape[1]:
-        raise ValueError("x and weight K differ")
-    acc = x @ w.T
-    v = np.asarray(x_scale, np.float64)[:, None] * np.asarray(w_scale_shard, np.float64)[None, :] * acc
-    if bias_shard_bits is not None:
-        b = bf16_to_f64(bias_shard_bits)
-        if b.shape != (total,):
-            raise ValueError(f"bias shard has {b.size} entries, expected {total}")
-        v = v + b[None, :]
-    a = f32(v)
+    if np.shape(wq_shard)[0] != total:
+        raise ValueError(f"weight shard has {np.shape(wq_shard)[0]} rows, shard total is {total}")
+    a = f32(linear_sums_fp8(xq, x_scale, wq_shard, w_scale_shard, bias_shard_bits))
     if act == ACT_GELU:
         a = f32(gelu_erf(a))
     y = bf16_round(a) if out_dtype == OUT_BF16 else a

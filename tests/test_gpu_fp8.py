@@ -1,7 +1,7 @@
 """fp8 prefill column linear on the GPU against the oracle: per-row E4M3 activation codes and
 scales bit for bit, the E4M3 x E4M3 product exact on integer codes with power-of-two scales,
-within tolerance on gaussian inputs with bias, GELU and LOGICAL placement, on both fp8 tiles,
-and on sampled rows of the RMSNorm workload's shape."""
+within the fp8 accumulation bound on gaussian inputs with bias, GELU and LOGICAL placement, on
+both fp8 tiles, and on every row of the RMSNorm workload's shape."""
 import numpy as np
 import pytest
 import torch
@@ -9,18 +9,17 @@ import torch
 import oracle
 import synth
 import tensor_transformer_linear_amd as tt
-from helpers import assert_close, dev_bf16, dev_f32, dev_u8, host_bits, host_f32
+from helpers import C_FP8, AbsSums, check_bf16, check_f32, dev_bf16, dev_f32, dev_u8, host_bits, host_f32
 
 pytestmark = pytest.mark.gpu
 
 TILES = [0, 2]  # 256x256 (ping-pong, 8 waves) and 128x128
 
-# The fp8 matrix instruction (v_mfma_f32_32x32x64_f8f6f4) sums its 64 products with about 16
-# significant bits (measured: 1.5e-5 rms and 1e-4 max of rms(ref) on gaussian operands, where
-# the bf16 instruction on the same values is at 4e-8). Well inside the 2e-2 * rms bound, but it
-# moves about 1 % of bf16 outputs across a rounding boundary: up to 5 % may sit one ulp off.
-FP8_STRADDLE = 0.05
-FP8_F32_TOL = 1e-3  # float32 outputs: max |err| <= 1e-3 * rms, a tighter guard on the product
+# The fp8 matrix instruction (v_mfma_f32_32x32x64_f8f6f4) sums its 64 products at reduced
+# precision inside the instruction; the tests hold its float32 sums to the wider accumulation
+# bound C_FP8 * sum|x w| (helpers), and bf16 outputs to straddles within that bound. About 1 %
+# of the bf16 outputs straddle (against 1e-4 with the bf16 instruction); FP8_SHARE caps that.
+FP8_SHARE = 0.05
 
 
 def _special_rows(K, seed):
@@ -107,7 +106,8 @@ def test_fp8_linear_gaussian_bias_gelu_logical(tile):
     rq, rs = oracle.quantize_rows_e4m3(x)
     assert np.array_equal(xq.cpu().numpy(), rq) and np.array_equal(xs.cpu().numpy(), rs)
     ref = oracle.column_linear_fp8(rq, rs, wq, ws, b, sizes, tp, rank, act=oracle.ACT_GELU)
-    assert_close(host_bits(y), ref, what="fp8 local", straddle=FP8_STRADDLE)
+    check_bf16(host_bits(y), ref, oracle.linear_sums_fp8(rq, rs, wq, ws, b), AbsSums.fp8(rq, rs, wq, ws, b), c=C_FP8,
+               gelu=True, what="fp8 local", share=FP8_SHARE)
     assert np.array_equal(host_bits(ylog)[:, rows], host_bits(y))   # LOGICAL = LOCAL scattered, bit for bit
 
 
@@ -124,8 +124,8 @@ def test_fp8_linear_f32_output_accuracy(tile):
                                     y_dtype=tt.TP_DTYPE_F32)
     finally:
         tt.set_gemm_tile(-1)
-    ref = oracle.column_linear_fp8(rq, rs, wq, ws, None, [N], 1, 0, out_dtype=oracle.OUT_F32)
-    assert_close(host_f32(y), ref, tol=FP8_F32_TOL, what="fp8 f32 out")
+    check_f32(host_f32(y), oracle.linear_sums_fp8(rq, rs, wq, ws), AbsSums.fp8(rq, rs, wq, ws).block(0, M), c=C_FP8,
+              what="fp8 f32 out")
 
 
 def test_fp8_linear_empty_input():
@@ -136,19 +136,31 @@ def test_fp8_linear_empty_input():
     assert y.shape == (0, 64)
 
 
-def test_fp8_prefill_workload4_shape_sampled_rows():
-    """The RMSNorm workload's column shard [3072, 8192] on its 32768 x rows, fp8: codes of the
-    sampled rows bit for bit, outputs within tolerance."""
+def test_fp8_prefill_workload4_shape_every_row():
+    """The RMSNorm workload's column shard [3072, 8192] on its 32768 x rows, fp8: the codes and
+    scales of every row bit for bit, every output within the fp8 rule; the bf16 output is the
+    rounding of the float32 output of the same launch."""
     c = synth.WORKLOADS[4]
     inp = synth.workload_inputs(4)
     x, w = inp["x"], inp["w"]
     wq, ws = synth.quantize_e4m3_channels(w)
     xq, xs = tt.tp_quantize_rows_e4m3(dev_bf16(x))
-    y = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), None, [c["out_logical"]], c["tp"], c["rank"])
-    g = np.random.default_rng(9)
-    sr = np.unique(np.concatenate([np.arange(8), np.arange(x.shape[0] - 8, x.shape[0]), g.integers(0, x.shape[0], 24)]))
-    rq, rs = oracle.quantize_rows_e4m3(x[sr])
-    idx = torch.from_numpy(sr).cuda()
-    assert np.array_equal(xq[idx].cpu().numpy(), rq) and np.array_equal(xs[idx].cpu().numpy(), rs)
-    ref = oracle.column_linear_fp8(rq, rs, wq, ws, None, [c["out_logical"]], c["tp"], c["rank"])
-    assert_close(host_bits(y[idx]), ref, what="fp8 workload-4 rows", straddle=FP8_STRADDLE)
+    sub = [c["out_logical"]]
+    y = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), None, sub, c["tp"], c["rank"])
+    y32 = tt.tp_column_linear_fp8(xq, xs, dev_u8(wq), dev_f32(ws), None, sub, c["tp"], c["rank"],
+                                  y_dtype=tt.TP_DTYPE_F32)
+    got, got32 = host_bits(y), host_f32(y32)
+    assert np.array_equal(got, host_bits(y32.to(torch.bfloat16)))
+    del y, y32
+    q_gpu, s_gpu = xq.cpu().numpy(), xs.cpu().numpy()
+    n = 0
+    for r0 in range(0, x.shape[0], 1024):
+        r1 = min(x.shape[0], r0 + 1024)
+        rq, rs = oracle.quantize_rows_e4m3(x[r0:r1])
+        assert np.array_equal(q_gpu[r0:r1], rq) and np.array_equal(s_gpu[r0:r1], rs), f"codes rows {r0}:{r1}"
+        v = oracle.linear_sums_fp8(rq, rs, wq, ws)
+        sums = AbsSums.fp8(rq, rs, wq, ws)
+        ref = oracle.column_linear_fp8(rq, rs, wq, ws, None, sub, c["tp"], c["rank"])
+        n += check_bf16(got[r0:r1], ref, v, sums, c=C_FP8, what=f"fp8 rows {r0}:{r1}", share=FP8_SHARE)
+        check_f32(got32[r0:r1], v, sums.block(0, r1 - r0), c=C_FP8, what=f"fp8 f32 rows {r0}:{r1}")
+    print(f"fp8 prefill: {n} rounding straddles of {got.size}")

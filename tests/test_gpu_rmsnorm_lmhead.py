@@ -6,17 +6,10 @@ import torch
 import oracle
 import synth
 import tensor_transformer_linear_amd as tt
-from helpers import argmax_ok, assert_close, dev_bf16, dev_f32, dev_u8, host_bits, host_f32
+from helpers import (AbsSums, admissible_rows, argmax_ok, assert_close, check_bf16, check_f32, check_rmsnorm_rows,
+                     dev_bf16, dev_f32, dev_u8, host_bits, host_f32)
 
 pytestmark = pytest.mark.gpu
-
-
-def _xnorm_agrees(got_bits, ref_bits):
-    """The normalised rows equal the oracle's except where the float32 row statistic's last
-    bit differs (float32 sums on the GPU, float64 in the oracle): one bf16 ulp, rarely."""
-    d = np.abs(got_bits.astype(np.int32) - ref_bits.astype(np.int32))
-    assert d.max() <= 1
-    assert np.count_nonzero(d) <= 1e-3 * d.size
 
 
 @pytest.mark.parametrize("K", [1024, 8192, 8200, 136])
@@ -33,12 +26,16 @@ def test_rmsnorm_column_linear(K, scaled):
     y_ws = tt.rmsnorm_column_linear(X, S, 1e-6, W, None, sizes, tp, rank)  # materialised in the workspace
     small = torch.empty(tt.tp_rmsnorm_workspace_min_bytes(M, K), dtype=torch.uint8, device="cuda")
     y_fused = tt.rmsnorm_column_linear(X, S, 1e-6, W, None, sizes, tp, rank, workspace=small)
-    ref_y, ref_xn = oracle.rmsnorm_column_linear(x, s, w_r, None, sizes, tp, rank)
-    _xnorm_agrees(host_bits(xn), ref_xn)
+    # the normalised rows: the oracle's, or rows whose factor took its other admissible rounding
+    ref_xn, other = check_rmsnorm_rows(host_bits(xn), x, s)
+    assert len(other) <= 2
+    a = admissible_rows(ref_xn, other, x, s)
+    ref_y = oracle.column_linear(a, w_r, None, sizes, tp, rank)
+    check_bf16(host_bits(y_mat), ref_y, oracle.linear_sums(a, w_r), AbsSums.bf16(a, w_r), what="rmsnorm column linear")
+    assert_close(host_bits(y_mat), oracle.rmsnorm_column_linear(x, s, w_r, None, sizes, tp, rank)[0], what="end to end")
     # the fused A-load normalisation computes the same bf16 operand as the materialised rows
     assert torch.equal(y_mat.view(torch.int16), y_fused.view(torch.int16))
     assert torch.equal(y_mat.view(torch.int16), y_ws.view(torch.int16))
-    assert_close(host_bits(y_fused), ref_y, what="rmsnorm column linear")
 
 
 def test_rmsnorm_special_rows():
@@ -64,11 +61,14 @@ def _lm_case(B, K, vocab, tp, rank, chunk, seed, fp8):
     if fp8:
         q, s = synth.quantize_e4m3_blocks(w)
         lg, idx, mx = tt.lm_head_shard_argmax(X, vocab, tp, rank, chunk, dev_u8(q), tt.TP_DTYPE_FP8_E4M3, dev_f32(s))
-        ref = oracle.lm_head_logits(x, w_fp8=q, w_scale=s, max_rows_per_chunk=chunk)
+        v = oracle.lm_head_sums(x, w_fp8=q, w_scale=s, max_rows_per_chunk=chunk)
+        wabs = np.abs(oracle.e4m3_to_f64(q) * np.repeat(s.astype(np.float64), 128, axis=1))
     else:
         lg, idx, mx = tt.lm_head_shard_argmax(X, vocab, tp, rank, chunk, dev_bf16(w))
-        ref = oracle.lm_head_logits(x, w, max_rows_per_chunk=chunk)
-    return lg, idx, mx, ref
+        v = oracle.lm_head_sums(x, w, max_rows_per_chunk=chunk)
+        wabs = np.abs(oracle.bf16_to_f64(w))
+    check_f32(host_f32(lg), v, np.abs(oracle.bf16_to_f64(x)) @ wabs.T, what="logits")
+    return lg, idx, mx, oracle.f32(v)
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -77,7 +77,6 @@ def _lm_case(B, K, vocab, tp, rank, chunk, seed, fp8):
 ])
 def test_lm_head_small(fp8, B, K, vocab, tp, rank, chunk):
     lg, idx, mx, ref = _lm_case(B, K, vocab, tp, rank, chunk, B + K, fp8)
-    assert_close(host_f32(lg), ref, what="logits")
     assert argmax_ok(idx.cpu().numpy(), ref) == []
     i = idx.cpu().numpy()
     assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])

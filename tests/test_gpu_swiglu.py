@@ -1,14 +1,16 @@
 """Fused q_wi projection with SwiGLU and the fused o_wo partial on the GPU against the oracle.
 
 * Integer inputs whose products and sums are exact in float32 and in bf16: the query columns
-  are bit-exact and the SwiGLU outputs may differ only where float32 and float64 evaluation of
-  the Swish straddle a bf16 rounding boundary (one ulp, rare). This pins the head map, the
-  gate/value pairing and the placement in y_fused, on every tile shape and both main loops.
-* Gaussian inputs: max|err| <= 2e-2 rms; wi0 and wi1 are rounded to bf16 before the SwiGLU,
-  so an accumulator that straddles a bf16 boundary moves the output by up to two ulps.
-* The o_wo partial (float32) and the whole chain q_wi -> SwiGLU -> o_wo.
+  are bit-exact and a SwiGLU output may differ only where float32 and float64 evaluation of
+  the Swish straddle a bf16 rounding boundary (helpers.check_swiglu). This pins the head map,
+  the gate/value pairing and the placement in y_fused, on every tile shape and both main loops.
+* Gaussian inputs: wi0 and wi1 are rounded to bf16 before the SwiGLU; an output that differs
+  from the oracle's must be the SwiGLU of gate and value roundings within the accumulation
+  bound of the exact sums.
+* The o_wo partial (float32, within the accumulation bound) and the whole chain
+  q_wi -> SwiGLU -> o_wo.
 * The full-size workload (8192 tokens, E 8192, 64 heads of 128, d_ff 32768, tp 8 rank 0),
-  checked on sampled rows.
+  every output checked.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ import torch
 import oracle
 import synth
 import tensor_transformer_linear_amd as tt
-from helpers import TOL, assert_close, dev_bf16, host_bits
+from helpers import AbsSums, assert_close, check_bf16, check_f32, check_swiglu, dev_bf16, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -42,14 +44,32 @@ def _exact_inputs(M, E, rows, seed):
     return x, w
 
 
-def _check_exact(q, y, att, q_ref, y_ref, what):
-    assert np.array_equal(q, q_ref), f"{what}: query columns differ"
+def _split_rows(heads, padded, qkv, ff, tp):
+    """Rows of the rank's q_wi weight that feed the query, gate and value columns, in output
+    column order (head-major)."""
+    h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
+    base = (np.arange(h_r) * qph)[:, None]
+    q_rows = (base + np.arange(qkv)[None, :]).reshape(-1)
+    g_rows = (base + qkv + np.arange(fph)[None, :]).reshape(-1)
+    return q_rows, g_rows, g_rows + fph
+
+
+def _check(x, w, dims, q, y, att, what, row0=0, q_ref=None, y_ref=None):
+    """Query columns bit-equal or checked straddles, SwiGLU outputs under check_swiglu, attention
+    slots untouched."""
+    heads, padded, qkv, ff, tp, rank = dims
+    if q_ref is None:
+        q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
+    qr, gr, ur = _split_rows(heads, padded, qkv, ff, tp)
+    v = oracle.linear_sums(x, w)
+    M = x.shape[0]
+    n = 0
+    if q is not None:
+        n += check_bf16(q.reshape(M, -1), q_ref.reshape(M, -1), v[:, qr], AbsSums.bf16(x, w[qr]), what=f"{what} q")
+    n += check_swiglu(y.reshape(M, -1), y_ref.reshape(M, -1), v[:, gr], v[:, ur], AbsSums.bf16(x, w[gr]),
+                      AbsSums.bf16(x, w[ur]), what=f"{what} swiglu")
     assert np.all(att == SENTINEL), f"{what}: attention slots were written"
-    d = np.abs(y.astype(np.int32) - y_ref.astype(np.int32))
-    same_sign = (y & 0x8000) == (y_ref & 0x8000)
-    off = d != 0
-    assert np.all(same_sign[off] & (d[off] == 1)), f"{what}: SwiGLU outputs more than one ulp off"
-    assert np.count_nonzero(off) <= 1e-3 * y.size + 1, f"{what}: {np.count_nonzero(off)} outputs one ulp off"
+    return n
 
 
 SHAPES = [
@@ -66,13 +86,12 @@ def test_qwi_swiglu_integer_exact(shape, tile):
     M, E, heads, padded, qkv, ff, tp, rank = shape
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x, w = _exact_inputs(M, E, h_r * qph, 7 * M + E)
-    q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
     tt.set_gemm_tile(tile)
     try:
         q, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank)
     finally:
         tt.set_gemm_tile(-1)
-    _check_exact(q, y, att, q_ref, y_ref, f"tile {tile} {shape}")
+    _check(x, w, shape[2:], q, y, att, f"tile {tile} {shape}")
 
 
 @pytest.mark.parametrize("shape", [(37, 40, 2, 0, 3, 10, 1, 0),     # E % 32 != 0: register-staged loop; fph 5
@@ -81,9 +100,8 @@ def test_qwi_swiglu_small_and_register_path(shape):
     M, E, heads, padded, qkv, ff, tp, rank = shape
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x, w = _exact_inputs(M, E, h_r * qph, 13 + E)
-    q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
     q, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank)
-    _check_exact(q, y, att, q_ref, y_ref, f"small {shape}")
+    _check(x, w, shape[2:], q, y, att, f"small {shape}")
 
 
 @pytest.mark.parametrize("path", [0, 1])
@@ -91,23 +109,20 @@ def test_qwi_swiglu_both_main_loops(path):
     M, E, heads, padded, qkv, ff, tp, rank = SHAPES[0]
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x, w = _exact_inputs(M, E, h_r * qph, 11)
-    q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
     tt.set_gemm_path(path)
     try:
         q, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank)
     finally:
         tt.set_gemm_path(-1)
-    _check_exact(q, y, att, q_ref, y_ref, f"path {path}")
+    _check(x, w, SHAPES[0][2:], q, y, att, f"path {path}")
 
 
 def test_qwi_swiglu_without_queries():
     M, E, heads, padded, qkv, ff, tp, rank = SHAPES[1]
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x, w = _exact_inputs(M, E, h_r * qph, 12)
-    _, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
     _, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank, with_q=False)
-    assert np.all(att == SENTINEL)
-    assert np.count_nonzero(y != y_ref) <= 1e-3 * y.size + 1
+    _check(x, w, SHAPES[1][2:], None, y, att, "without queries")
 
 
 @pytest.mark.parametrize("shape", SHAPES[:2])
@@ -116,11 +131,8 @@ def test_qwi_swiglu_gaussian(shape):
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x = synth.bf16_normal((M, E), 1.0, 60, 0)
     w = synth.bf16_normal((h_r * qph, E), 0.02, 60, 1)
-    q_ref, y_ref = oracle.qwi_swiglu(x, w, heads, padded, qkv, ff, tp, rank)
     q, y, att = _run(x, w, heads, padded, qkv, ff, tp, rank)
-    assert np.all(att == SENTINEL)
-    assert_close(q, q_ref, what="q")
-    assert_close(y, y_ref, what="swiglu", straddle=5e-3, ulps=2)
+    _check(x, w, shape[2:], q, y, att, f"gaussian {shape}")
 
 
 def test_padded_heads_are_zero():
@@ -152,7 +164,9 @@ def test_o_wo_partial(tile):
         torch.cuda.synchronize()
     finally:
         tt.set_gemm_tile(-1)
-    assert_close(out.cpu().numpy(), ref, tol=1e-4, what="o_wo partial")
+    yf2 = yf.reshape(M, -1)
+    check_f32(out.cpu().numpy(), oracle.linear_sums(yf2, w_o), AbsSums.bf16(yf2, w_o).block(0, M), what="o_wo partial",
+              ref=ref)
 
 
 def test_o_wo_rank_ordered_sum():
@@ -190,28 +204,36 @@ def test_chain_qwi_swiglu_o_wo():
     assert_close(out.cpu().numpy(), ref, what="q_wi -> SwiGLU -> o_wo")
 
 
-def test_full_size_sampled_rows():
-    """8192 tokens, E 8192, 64 heads of 128, d_ff 32768, tp 8 rank 0: all outputs computed on
-    the GPU, sampled rows checked against the oracle."""
+def test_full_size_every_row():
+    """8192 tokens, E 8192, 64 heads of 128, d_ff 32768, tp 8 rank 0: every query column and
+    SwiGLU output checked; then the o_wo partial of the whole fused layer, checked against the
+    oracle's chain (its own SwiGLU outputs), the window widened where a SwiGLU output of the
+    GPU was an accepted other rounding."""
     M, E, heads, padded, qkv, ff, tp, rank = 8192, 8192, 64, 0, 128, 32768, 8, 0
+    dims = (heads, padded, qkv, ff, tp, rank)
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     x = synth.bf16_normal((M, E), 1.0, 65, 0)
     w = synth.bf16_normal((h_r * qph, E), 0.02, 65, 1)
     w_o = synth.bf16_normal((E, h_r * (qkv + fph)), 0.02, 65, 2)
-    xd, wd, wod = dev_bf16(x), dev_bf16(w), dev_bf16(w_o)
-    yf = torch.zeros((M, h_r, qkv + fph), dtype=torch.bfloat16, device="cuda")
+    y_att = synth.bf16_normal((M, h_r, qkv), 1.0, 65, 3)
+    yf = dev_bf16(np.concatenate([y_att, np.full((M, h_r, fph), SENTINEL, np.uint16)], axis=2))
     q = torch.empty((M, h_r, qkv), dtype=torch.bfloat16, device="cuda")
-    tt.tp_qwi_swiglu(xd, heads, padded, qkv, ff, tp, rank, wd, yf, q=q)
-    out = tt.tp_o_wo_partial(yf.view(M, -1), heads, padded, qkv, ff, tp, rank, wod)
+    tt.tp_qwi_swiglu(dev_bf16(x), heads, padded, qkv, ff, tp, rank, dev_bf16(w), yf, q=q)
+    out = tt.tp_o_wo_partial(yf.view(M, -1), heads, padded, qkv, ff, tp, rank, dev_bf16(w_o))
     torch.cuda.synchronize()
-    rows = np.random.default_rng(66).choice(M, 24, replace=False)
-    rows[:2] = [0, M - 1]
-    q_ref, y_ref = oracle.qwi_swiglu(x[rows], w, heads, padded, qkv, ff, tp, rank)
-    qb, yb = host_bits(q)[rows], host_bits(yf)[rows]
-    assert_close(qb, q_ref, what="q (sampled rows)")
-    assert_close(yb[:, :, qkv:], y_ref, what="swiglu (sampled rows)", straddle=5e-3, ulps=2)
-    assert not np.any(oracle.bf16_to_f64(yb[:, :, :qkv])), "attention slots were written"
-    # the o_wo partial from the GPU's own y_fused rows: the projection alone
-    ref = oracle.o_wo_partial(yb, w_o)
-    assert_close(out.cpu().numpy()[rows], ref, tol=1e-4, what="o_wo (sampled rows)")
-    assert TOL == 2e-2
+    qb, yb, ob = host_bits(q), host_bits(yf), out.cpu().numpy()
+    del q, yf, out
+    assert np.array_equal(yb[:, :, :qkv], y_att), "attention slots were written"
+    wo_abs = np.abs(oracle.bf16_to_f64(w_o))
+    n = 0
+    for r0 in range(0, M, 1024):
+        r1 = r0 + 1024
+        xb = x[r0:r1]
+        q_ref, y_ref = oracle.qwi_swiglu(xb, w, heads, padded, qkv, ff, tp, rank)
+        n += _check(xb, w, dims, qb[r0:r1], yb[r0:r1, :, qkv:], np.full(1, SENTINEL), f"rows {r0}:{r1}",
+                    q_ref=q_ref, y_ref=y_ref)
+        fused = oracle.fuse_heads(y_att[r0:r1], y_ref).reshape(r1 - r0, -1)
+        d = np.abs(oracle.bf16_to_f64(yb[r0:r1].reshape(r1 - r0, -1)) - oracle.bf16_to_f64(fused))
+        check_f32(ob[r0:r1], oracle.linear_sums(fused, w_o), AbsSums.bf16(fused, w_o).block(0, r1 - r0),
+                  what=f"o_wo rows {r0}:{r1}", ref=oracle.o_wo_partial(fused, w_o), extra=d @ wo_abs.T)
+    print(f"fused layer: {n} outputs differ from the oracle's, all checked straddles")

@@ -133,17 +133,46 @@ def test_channel_quantised_weights_decode_within_half_a_step():
     assert np.array_equal(q, oracle.e4m3_encode((wf / s[:, None]).astype(np.float32)))
 
 
-def test_tolerance_helper_accepts_rare_one_ulp_straddles_only():
+def test_straddle_rule_accepts_only_roundings_within_the_accumulation_bound():
+    """The GPU tests' acceptance rule for bf16 outputs (helpers.check_bf16): an output one unit
+    away from the oracle's is accepted only where the exact sum lies within the accumulation
+    bound of the bf16 rounding boundary between the two."""
     import helpers
-    ref = synth.bf16_normal((100, 100), 1.0, 904, 0)
+    def b(v):
+        return int(oracle.bf16_round(np.float32(v))[0])
+    # row 0: 1 + 2^-8 + 2^-20, a hair above the midpoint of 1.0 and 1.0078125 -> the oracle rounds up
+    # row 1: 1.25: far from any boundary
+    x = np.array([[b(1), b(1), b(2.0 ** -20)], [b(1.25), 0, 0]], dtype=np.uint16)
+    w = np.array([[b(1), b(2.0 ** -8), b(1)], [b(1), b(1), b(1)]], dtype=np.uint16)
+    v = oracle.linear_sums(x, w)
+    ref = oracle.column_linear(x, w, None, [2], 1, 0)
+    assert v[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -20 and oracle.bf16_to_f64(ref[0, 0]) == 1.0078125
+    sums = helpers.AbsSums.bf16(x, w)
+    assert helpers.check_bf16(ref, ref, v, sums) == 0
     got = ref.copy()
-    got.flat[[3, 77]] += 1                       # two rounding straddles: accepted
-    helpers.assert_close(got, ref)
-    bad = ref.copy()
-    bad.flat[5] ^= 0x4000                         # a large error elsewhere: rejected
+    got[0, 0] -= 1                                 # the other side of the boundary: a straddle
+    assert helpers.check_bf16(got, ref, v, sums) == 1
+    far = ref.copy()
+    far[1, 0] += 1                                 # one unit off, nowhere near a boundary
+    with pytest.raises(AssertionError, match="not rounding straddles"):
+        helpers.check_bf16(far, ref, v, sums)
+    with pytest.raises(AssertionError, match="not rounding straddles"):  # the straddle window is narrow
+        helpers.check_bf16(got, ref, v, sums, c=2.0 ** -30)
+    big = ref.copy()
+    big[1, 1] ^= 0x4000
     with pytest.raises(AssertionError):
-        helpers.assert_close(bad, ref)
-    many = ref.copy()
-    many.flat[:50] += 1                           # 0.5 % of outputs one ulp off: rejected
-    with pytest.raises(AssertionError):
-        helpers.assert_close(many, ref)
+        helpers.check_bf16(big, ref, v, sums)
+
+
+def test_f32_rule_holds_each_output_to_the_accumulation_bound():
+    import helpers
+    g = np.random.default_rng(3)
+    x = synth.bf16_from_float(g.standard_normal((8, 512)))
+    w = synth.bf16_from_float(g.standard_normal((16, 512)) * 0.02)
+    v = oracle.linear_sums(x, w)
+    sums = helpers.AbsSums.bf16(x, w).block(0, 8)
+    helpers.check_f32(oracle.f32(v), v, sums)
+    off = oracle.f32(v).astype(np.float64)
+    off[3, 4] += 4e-3 * sums[3, 4] * 2.0 ** -10
+    with pytest.raises(AssertionError, match="beyond the accumulation bound"):
+        helpers.check_f32(off, v, sums)
