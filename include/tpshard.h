@@ -301,7 +301,8 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
                           size_t workspace_bytes, void* stream);
 
 /*
- * tp_lm_head_workspace_bytes - device workspace lm_head_shard_argmax needs.
+ * tp_lm_head_workspace_bytes - device workspace lm_head_shard_argmax needs (enough for any
+ * batch size up to B and any of the library's launch shapes; 0 for invalid arguments).
  */
 TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk);
 
@@ -327,8 +328,9 @@ TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, 
  * workspace         device, tp_lm_head_workspace_bytes(...) bytes, 256-byte aligned; needs
  *                   no initialisation (per-workgroup argmax candidates, scratch between
  *                   calls). Calls that overlap in time must not share a workspace.
- * Two kernels run per 32 batch rows: the logits with per-workgroup argmax candidates,
- * then the candidates' reduction.
+ * Two kernels run per pass over the weight: the logits with per-workgroup argmax candidates,
+ * then the candidates' reduction. A pass takes up to 32 batch rows, or up to 64 when the call
+ * has more than 32 (then x stays in LDS and the weight streams once per 64 rows).
  * Errors: TP_ERR_INVALID_ARG, TP_ERR_SHAPE (chunk size <= 0, workspace short),
  * TP_ERR_UNSUPPORTED (K % 8, fp8 with K % 128, dtype), TP_ERR_HIP.
  */

@@ -515,7 +515,8 @@ def lm_head_shard_argmax(x, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w
 GEMM_PATH_AUTO, GEMM_PATH_REGISTER, GEMM_PATH_DMA = -1, 0, 1
 
 LM_HEAD_SHAPES = {0: (4, 8, 8, 1), 1: (2, 8, 8, 1), 2: (4, 4, 8, 1), 3: (2, 4, 8, 1), 4: (4, 8, 4, 1),
-                  5: (1, 8, 8, 1), 6: (8, 8, 4, 2), 7: (8, 4, 4, 2), 8: ("lds-ring", 64), 9: ("lds-ring", 128)}
+                  5: (1, 8, 8, 1), 6: (8, 8, 4, 2), 7: (8, 4, 4, 2), 8: ("lds-ring", 64), 9: ("lds-ring", 128),
+                  10: ("x-resident", 64)}
 
 
 def gemm_pick_tile(M: int, N: int, K: int) -> int:

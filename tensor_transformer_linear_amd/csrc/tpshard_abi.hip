@@ -398,7 +398,8 @@ int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int
   if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   const int64_t V_r = width_of(vocab, tp_size, rank);
   const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
-  const size_t need = tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
+  const size_t need = tpk::lm_head_shape_workspace_bytes(tune.lm_shape, (int)B, (int)V_r, (int)K,
+                                                        w_dtype == TP_DTYPE_FP8_E4M3, (int)chunk);
   if (workspace_bytes < need) return fail(TP_ERR_SHAPE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
 
   tpk::LmHeadProblem p;

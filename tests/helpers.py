@@ -244,3 +244,39 @@ def check_swiglu(gpu_bits, ref_bits, gate_v, value_v, gate_sums, value_sums, c=C
     same = g == r
     assert_close(np.where(same, g, r), r, tol, what)
     return int(diff.shape[0])
+
+
+def check_rmsnorm_rows(xn_gpu, x, s, r0=0):
+    """The GPU's normalised rows equal the oracle's, except rows whose factor r took the other
+    admissible float32 rounding: the GPU sums the squares in float32 pieces of K / 256 values
+    (relative error below (K / 256) 2^-24 on the mean square, half that on the factor), so a
+    float32 value that close to the exact factor may be its r. Returns ``(oracle rows, {row: r})``
+    for the rows that took another admissible value."""
+    ref, r_o = oracle.rmsnorm(x, s)
+    window = (x.shape[1] / 256 + 2) * 2.0 ** -24
+    bad = np.nonzero(np.any(xn_gpu != ref, axis=1))[0]
+    other = {}
+    if bad.size:
+        rho = oracle.rmsnorm_factor(x[bad])
+        for i, b in enumerate(bad):
+            found = None
+            for dr in (-1, 1):
+                cand = np.array([np.nextafter(r_o[b], np.float32(np.inf) if dr > 0 else np.float32(-np.inf))],
+                                dtype=np.float32)
+                if abs(float(cand[0]) - rho[i]) > window * rho[i]:
+                    continue
+                y, _ = oracle.rmsnorm(x[b:b + 1], s, r=cand)
+                if np.array_equal(y[0], xn_gpu[b]):
+                    found = cand
+            assert found is not None, f"normalised row {r0 + b} is not the oracle's for any admissible factor"
+            other[int(b)] = found
+    return ref, other
+
+
+def admissible_rows(xn_ref, other, x, s):
+    """The oracle's normalised rows, with the rows in ``other`` (``check_rmsnorm_rows``) taken
+    with their other admissible factor."""
+    a = xn_ref.copy()
+    for b, r in other.items():
+        a[b] = oracle.rmsnorm(x[b:b + 1], s, r=r)[0][0]
+    return a

@@ -152,7 +152,7 @@ def test_lm_head_every_launch_shape(shape, fp8):
         tt.set_lm_head_shape(-1)
 
 
-@pytest.mark.parametrize("shape", [8, 9])
+@pytest.mark.parametrize("shape", [8, 9, 10])
 @pytest.mark.parametrize("B,K", [(40, 256), (3, 96), (9, 200)])
 def test_lm_head_lds_ring_batch_passes_and_ragged_k(shape, B, K):
     """The LDS-ring kernels over two 32-row batch passes, and with a bf16 K that their stage
@@ -164,5 +164,22 @@ def test_lm_head_lds_ring_batch_passes_and_ragged_k(shape, B, K):
             lg, idx, mx, ref = _lm_case(B, K, 2 * 1000 + 37, 2, 1, 500, 90 + shape, fp8)
             assert_close(host_f32(lg), ref, what=f"shape {shape} fp8 {fp8}")
             assert argmax_ok(idx.cpu().numpy(), ref) == []
+    finally:
+        tt.set_lm_head_shape(-1)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("B,K,vocab", [(1, 4096, 8 * 1000 + 13), (32, 1536, 2 * 700 + 1), (33, 4096, 2 * 1000 + 37),
+                                       (64, 640, 8 * 333), (100, 1280, 2 * 129), (5, 128, 2 * 70)])
+def test_lm_head_x_resident_slices_and_batch_passes(fp8, B, K, vocab):
+    """The x-resident kernel: x slices of 1024 (32-row passes) or 512 (64-row passes) columns,
+    with a ragged last slice (K = 1536, 640, 1280, 128), one 32-row pass, one 64-row pass (33 and
+    64 rows), two passes (100 rows), a single row, vocab shards that end inside a 64-row tile."""
+    tt.set_lm_head_shape(10)
+    try:
+        lg, idx, mx, ref = _lm_case(B, K, vocab, 2 if vocab % 8 else 8, 1, 500, 110 + B, fp8)
+        assert argmax_ok(idx.cpu().numpy(), ref) == []
+        i = idx.cpu().numpy()
+        assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])
     finally:
         tt.set_lm_head_shape(-1)

@@ -176,3 +176,36 @@ def test_f32_rule_holds_each_output_to_the_accumulation_bound():
     off[3, 4] += 4e-3 * sums[3, 4] * 2.0 ** -10
     with pytest.raises(AssertionError, match="beyond the accumulation bound"):
         helpers.check_f32(off, v, sums)
+
+
+def test_swiglu_rule_accepts_only_admissible_gate_value_roundings():
+    """helpers.check_swiglu: the GPU's SwiGLU output must be the rounding of swish(g) * u for bf16
+    g, u within the accumulation bound of the exact sums; a value that moved although neither sum
+    is near a bf16 boundary is rejected, one whose value sum sits on a boundary is accepted."""
+    import helpers
+
+    def b(v):
+        return int(oracle.bf16_round(np.float32(v))[0])
+    # row 0: gate 1, value 1 + 2^-8 + 2^-20 (a hair above the midpoint of 1 and 1.0078125);
+    # row 1: gate 2, value 1.25, far from any boundary
+    x = np.array([[b(1), b(1), b(2.0 ** -20)], [b(1), 0, 0]], dtype=np.uint16)
+    wg = np.array([[b(1), 0, 0], [b(2), 0, 0]], dtype=np.uint16)[[0, 0]]
+    wu = np.array([[b(1), b(2.0 ** -8), b(1)]], dtype=np.uint16)
+    # one head, qkv 0: gate rows [g], value rows [u]; columns: the two rows of x against one gate/value
+    gate = oracle.linear_sums(x, wg[:1])
+    value = oracle.linear_sums(x, wu)
+    gb = oracle.bf16_round(oracle.f32(gate))
+    ub = oracle.bf16_round(oracle.f32(value))
+    ref = oracle.bf16_round(oracle.f32(oracle.swish(oracle.bf16_to_f64(gb)) * oracle.bf16_to_f64(ub)))
+    gs, us = helpers.AbsSums.bf16(x, wg[:1]), helpers.AbsSums.bf16(x, wu)
+    assert helpers.check_swiglu(ref, ref, gate, value, gs, us) == 0
+    # row 0 with the value rounded down instead (1.0): an admissible other rounding
+    alt = ref.copy()
+    alt[0, 0] = oracle.bf16_round(oracle.f32(oracle.swish(oracle.bf16_to_f64(gb[0, 0])) * 1.0))[0]
+    assert alt[0, 0] != ref[0, 0]
+    assert helpers.check_swiglu(alt, ref, gate, value, gs, us) == 1
+    # row 1 one unit off: its sums are far from any boundary
+    bad = ref.copy()
+    bad[1, 0] += 1
+    with pytest.raises(AssertionError, match="not roundings"):
+        helpers.check_swiglu(bad, ref, gate, value, gs, us)
