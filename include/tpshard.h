@@ -340,6 +340,25 @@ TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t voc
                          size_t workspace_bytes, void* stream);
 
 /*
+ * lm_head_shard_argmax_noalloc - lm_head_shard_argmax for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same results bit for bit.
+ *
+ * The per-workgroup candidates go to a device array of 1 MiB inside the library, one copy per
+ * GPU, which the library holds until the process ends (its address is looked up on the first
+ * call on each device). The call allocates nothing. Shards whose candidates do not fit (more
+ * than 262144 vocab rows, or 131072 when more than 32 batch rows share a weight pass) return
+ * TP_ERR_SHAPE before anything is enqueued. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other threads) race and must be ordered by
+ * the caller. Nothing in the array needs initialisation. Errors: as lm_head_shard_argmax, and
+ * TP_ERR_HIP when the array's address cannot be found.
+ */
+TP_API int lm_head_shard_argmax_noalloc(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                                        int64_t max_rows_per_chunk, const void* w_shard, int w_dtype,
+                                        const float* w_block_scale, float* logits, int32_t* argmax_local,
+                                        float* max_logit, void* stream);
+
+/*
  * tp_last_error - message of the last non-OK status returned on the calling thread
  * ("" if none). The pointer stays valid until the thread's next call into the library.
  */

@@ -56,6 +56,8 @@ SIGNATURES = {
     "tp_lm_head_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _i64]),
     "lm_head_shard_argmax": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _int, _vp, _vp, _vp, _vp, _vp,
                                     _sz, _vp]),
+    "lm_head_shard_argmax_noalloc": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _int, _vp, _vp, _vp, _vp,
+                                            _vp]),
     "tp_last_error": (ctypes.c_char_p, []),
     "tp_version": (ctypes.c_char_p, []),
 }
@@ -509,6 +511,32 @@ def lm_head_shard_argmax(x, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w
     _call("lm_head_shard_argmax", _ptr(x), B, K, vocab, tp_size, rank, max_rows_per_chunk, _ptr(w_shard), w_dtype,
           _ptr(w_block_scale), _ptr(logits), _ptr(argmax_local), _ptr(max_logit), _ptr(workspace),
           workspace.numel(), _stream(stream))
+    return logits, argmax_local, max_logit
+
+
+def lm_head_shard_argmax_noalloc(x, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w_dtype=TP_DTYPE_BF16,
+                                 w_block_scale=None, logits=None, argmax_local=None, max_logit=None, stream=None):
+    """``lm_head_shard_argmax`` with the library's own device scratch instead of a workspace (for
+    callers that cannot allocate: pass every output); returns (logits, idx, max)."""
+    _tensor(x, "x", _BF16, (None, None))
+    B, K = x.shape
+    v_r, _ = _shard_total([vocab], tp_size, rank)
+    _tensor(w_shard, "w_shard", _E4M3 if w_dtype == TP_DTYPE_FP8_E4M3 else _BF16, (v_r, K))
+    if w_block_scale is not None:
+        _tensor(w_block_scale, "w_block_scale", (torch.float32,), (v_r, K // 128))
+    for name, t, shape, dts in (("logits", logits, (B, v_r), (torch.float32,)),
+                                ("argmax_local", argmax_local, (B,), (torch.int32,)),
+                                ("max_logit", max_logit, (B,), (torch.float32,))):
+        if t is not None:
+            _tensor(t, name, dts, shape)
+    dev = _same_gpu(x=x, w_shard=w_shard, w_block_scale=w_block_scale, logits=logits, argmax_local=argmax_local,
+                    max_logit=max_logit)
+    if logits is None:
+        logits = torch.empty((B, v_r), dtype=torch.float32, device=dev)
+    if argmax_local is None:
+        argmax_local = torch.empty((B,), dtype=torch.int32, device=dev)
+    _call("lm_head_shard_argmax_noalloc", _ptr(x), B, K, vocab, tp_size, rank, max_rows_per_chunk, _ptr(w_shard),
+          w_dtype, _ptr(w_block_scale), _ptr(logits), _ptr(argmax_local), _ptr(max_logit), _stream(stream))
     return logits, argmax_local, max_logit
 
 

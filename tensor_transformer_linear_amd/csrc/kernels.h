@@ -116,6 +116,9 @@ struct LmHeadProblem {
 size_t lm_head_workspace_bytes(int B, int V, int chunk);  // the largest need over the launch shapes
 // The workspace one launch shape needs (-1: the default shape).
 size_t lm_head_shape_workspace_bytes(int shape, int B, int V, int K, bool fp8, int chunk);
+// This GPU's device scratch for the allocation-free entry point (its address, found once per
+// device with the device current) and its size.
+hipError_t lm_head_scratch(void** ptr, size_t* bytes);
 int lm_head_shape_count();
 // shape: -1 = default launch shape, else an index into the LM head's shape table (tuning).
 hipError_t launch_lm_head(const LmHeadProblem& p, int shape, hipStream_t stream);

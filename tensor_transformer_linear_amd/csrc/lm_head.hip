@@ -32,6 +32,9 @@
 // with scale 1: exact, every E4M3 value is a bf16 value) and each 128-wide K
 // block's partial is multiplied by the row's block scale before it joins the
 // float32 accumulator.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -982,6 +985,37 @@ size_t lm_head_workspace_bytes(int B, int V, int chunk) {
   // the x-resident kernel: candidates of up to 64 batch rows per 64-row tile
   need = max(need, (size_t)((V + LMX_ROWS - 1) / LMX_ROWS) * 64 * (sizeof(float) + sizeof(int)));
   return need;
+}
+
+// The allocation-free entry point's workspace: a file-scope device array of
+// kLmScratchBytes, one copy per GPU, held until the process ends. Host code never names the
+// array as an address: its device address is looked up once per device, with that device
+// current, and kept.
+constexpr size_t kLmScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kLmScratchBytes];
+
+hipError_t lm_head_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* a = addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    a = addr[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (a == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *ptr = a;
+  *bytes = kLmScratchBytes;
+  return hipSuccess;
 }
 
 hipError_t launch_lm_head(const LmHeadProblem& p, int shape, hipStream_t stream) {

@@ -590,4 +590,33 @@ TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t voc
                                      tpabi::Tuning{});
 }
 
+TP_API int lm_head_shard_argmax_noalloc(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
+                                        int64_t max_rows_per_chunk, const void* w_shard, int w_dtype,
+                                        const float* w_block_scale, float* logits, int32_t* argmax_local,
+                                        float* max_logit, void* stream) {
+  // the sizes are checked by the shared body; the scratch must hold this call's candidates
+  if (B >= 1 && B <= INT_MAX && K >= 1 && K <= INT_MAX && vocab >= 1 && vocab <= INT_MAX && tp_size >= 1 &&
+      rank >= 0 && rank < tp_size && vocab >= tp_size && max_rows_per_chunk >= 1) {
+    const int64_t V_r = width_of(vocab, tp_size, rank);
+    const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
+    const size_t need = tpk::lm_head_shape_workspace_bytes(-1, (int)B, (int)V_r, (int)K, w_dtype == TP_DTYPE_FP8_E4M3,
+                                                          (int)chunk);
+    void* ws = nullptr;
+    size_t cap = 0;
+    const hipError_t e = tpk::lm_head_scratch(&ws, &cap);
+    if (e != hipSuccess) return hip_status(e, "lm_head_shard_argmax_noalloc scratch address");
+    if (need > cap)
+      return fail(TP_ERR_SHAPE, "the shard's %lld rows need %zu bytes of scratch; the library holds %zu per GPU",
+                  (long long)V_r, need, cap);
+    return tpabi::lm_head_shard_argmax(x, B, K, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w_dtype,
+                                       w_block_scale, logits, argmax_local, max_logit, ws, cap, stream,
+                                       tpabi::Tuning{});
+  }
+  // invalid sizes: the shared body reports them before it looks at the workspace (a stand-in
+  // address of zero bytes, never dereferenced: a zero-byte workspace fails its size check)
+  return tpabi::lm_head_shard_argmax(x, B, K, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w_dtype,
+                                     w_block_scale, logits, argmax_local, max_logit, reinterpret_cast<void*>(256), 0,
+                                     stream, tpabi::Tuning{});
+}
+
 }  // extern "C"
