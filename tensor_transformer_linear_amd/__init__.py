@@ -83,6 +83,7 @@ TUNING_SIGNATURES = {
     **{_tuning_name(n): (SIGNATURES[n][0], SIGNATURES[n][1] + [_int] * len(c)) for n, c in TUNING_CHOICES.items()},
     "tpt_gemm_pick_tile": (_int, [_i64, _i64, _i64]),
     "tpt_lm_head_shape_count": (_int, []),
+    "tpt_mfma_row_sums": (_int, [_int, _vp, _vp, _vp, _vp]),
     "tp_last_error": (ctypes.c_char_p, []),
 }
 

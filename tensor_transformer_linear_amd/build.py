@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 TUNING_LIB = os.path.join(PKG, "libtpshard_tuning.so")
 SOURCES = ["tpshard_abi.hip", "gemm.hip", "rmsnorm.hip", "lm_head.hip", "quant.hip", "embed.hip", "reduce.hip"]
-TUNING_SOURCES = ["tuning_abi.hip"]
+TUNING_SOURCES = ["tuning_abi.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -56,6 +56,12 @@ TP_API int tpt_lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t
 TP_API int tpt_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
 TP_API int tpt_lm_head_shape_count(void);
 
+/* One matrix instruction on fixed operands, to observe its rounding: A holds 32 rows (fp8 = 0:
+ * [32][16] bf16 values; fp8 = 1: [32][64] E4M3 codes), B is all ones and C[i] is added to row
+ * i, so out[i] = C[i] + the sum of row i's values as the instruction computes it (one wave;
+ * a: device, 16-byte aligned; c, out: device f32 [32]). TP_ERR_HIP for a failed launch. */
+TP_API int tpt_mfma_row_sums(int fp8, const void* a, const float* c, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -167,7 +167,8 @@ def check_f32(gpu, exact, abs_sums_block, c=C_BF16, what="", tol=TOL, ref=None, 
     sums everywhere (``abs_sums_block`` is the full ``sum|x w|`` array of the block), and the
     float tolerance against the oracle's float32 output ``ref`` (default: f32(exact)).
     ``extra`` widens the bound where the GPU's input differed from the oracle's by accepted
-    straddles (``sum_k |d_k w_k|`` of those differences)."""
+    straddles (``sum_k |d_k w_k|`` of those differences). Returns the largest
+    ``|gpu - exact| / sum|x w|`` (the measured accumulation error against the bound's scale)."""
     g = np.asarray(gpu, dtype=np.float64)
     v = np.asarray(exact, dtype=np.float64)
     e = acc_bound(np.asarray(abs_sums_block), v, c)
@@ -179,6 +180,8 @@ def check_f32(gpu, exact, abs_sums_block, c=C_BF16, what="", tol=TOL, ref=None, 
         raise AssertionError(f"{what}: {int(over.sum())} float32 outputs beyond the accumulation bound; first at "
                              f"{k}: gpu {g[k]!r}, exact {v[k]!r}, bound {e[k]:.3g}")
     assert_close(g, oracle.f32(v) if ref is None else ref, tol, what)
+    a = np.asarray(abs_sums_block, dtype=np.float64)
+    return float(np.max(np.abs(g - v) / np.where(a > 0, a, 1.0), initial=0.0))
 
 
 def argmax_ok(gpu_idx, ref_logits, tol=TOL):
