@@ -6,27 +6,29 @@
 // logits. Decode has a few batch rows, so the work is a stream of the weight
 // shard from HBM: every weight byte is read once.
 //
-// Two streaming kernels compute the logits; both give a workgroup a tile of weight
-// rows and finish with that workgroup's (max, lowest index) candidate per batch
-// row, which a second kernel launched right after reduces
-// (a kernel boundary instead of per-workgroup device-scope fences, which on gfx950
-// write back and invalidate the whole L2).
+// Four streaming kernels compute the logits; each gives a workgroup a tile of weight rows
+// and finishes with that workgroup's (max, lowest index) candidate per batch row, which a
+// second kernel launched right after reduces (a kernel boundary instead of per-workgroup
+// device-scope fences, which on gfx950 write back and invalidate the whole L2).
 //
-// * Register streaming (shapes 0-7): a workgroup owns 16 G weight rows and its
-//   waves split K; each wave loads the 16-byte pieces of its K steps straight into
-//   MFMA operand registers, P steps per batch, and the waves' partials are summed
-//   through LDS in wave order. Works for any K % 8 == 0.
-// * LDS ring (shapes 8, 9; the default): a workgroup owns 64 rows over the whole
-//   K; weight, x and block-scale pieces go global -> LDS with global_load_lds into
-//   a ring of stages that fills the CU's LDS, so the prefetch depth costs no
-//   registers. Needs K % 32 (64-byte stages) or K % 64 (128-byte stages) for bf16.
-//   Its tiles are whole 64-row blocks of the shard: the chunks only group the
-//   concatenated output, which is the same rows in the same order, so a chunk
-//   boundary inside a block changes nothing.
+// * Row-quad (shapes 11-15; the default): a workgroup owns 64 rows over the whole K, x sits
+//   in LDS one slice at a time (32 or 64 batch rows per pass), and each weight load
+//   instruction reads 4 rows x 256 contiguous bytes into registers; each wave turns its
+//   loads into the MFMA operand layout through 4 KB of its own LDS.
+// * x-resident (shape 10): the same split with the weight loaded straight in the operand
+//   layout (16 rows x 64 bytes per load instruction).
+// * LDS ring (shapes 8, 9; the fallback for a K the others cannot take): a workgroup owns 64
+//   rows over the whole K; weight, x and block-scale pieces go global -> LDS with
+//   global_load_lds into a ring of stages that fills the CU's LDS.
+// * Register streaming (shapes 0-7; any K % 8 == 0): a workgroup owns 16 G weight rows and
+//   its waves split K; each wave loads its K steps straight into MFMA operand registers and
+//   the waves' partials are summed through LDS in wave order.
 //
-// The register-streaming shapes tile each chunk on its own.
+// The 64-row kernels tile the shard in whole 64-row blocks: the chunks only group the
+// concatenated output, which is the same rows in the same order, so a chunk boundary inside
+// a block changes nothing. The register-streaming shapes tile each chunk on its own.
 //
-// Both multiply with v_mfma_f32_16x16x32_bf16, x as the row operand and the
+// All multiply with v_mfma_f32_16x16x32_bf16, x as the row operand and the
 // weight as the column operand, so every lane's accumulators belong to one weight
 // row. E4M3 weights are widened to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8
 // with scale 1: exact, every E4M3 value is a bf16 value) and each 128-wide K
@@ -34,6 +36,7 @@
 // float32 accumulator.
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -57,7 +60,8 @@ constexpr LmShape kLmShapes[] = {{4, 8, 8, 1}, {2, 8, 8, 1}, {4, 4, 8, 1}, {2, 4
                                  {4, 8, 4, 1}, {1, 8, 8, 1}, {4, 8, 4, 2}, {8, 4, 4, 2}};
 constexpr int kLmDmaShape = 8;  // 8, 9: the direct-to-LDS kernel (indices past the table)
 constexpr int kLmXresShape = 10;  // the x-resident kernel (batch passes of up to 64 rows)
-constexpr int kLmDefaultShape = 9;  // LDS ring, 128-byte stages (falls back to 4 for a ragged bf16 K)
+constexpr int kLmQuadShape = 11;  // 11 .. 15: the row-quad kernel (batch passes of 32 rows)
+constexpr int kLmRingShape = 9;  // LDS ring, 128-byte stages (falls back to 4 for a ragged bf16 K)
 
 // Two E4M3 codes (bytes HI ? 2,3 : 0,1 of w) -> two bf16, exactly (scale 1).
 template <bool HI>
@@ -572,6 +576,53 @@ struct LmxShape {
 constexpr int LMX_ROWS = 64;
 constexpr int LMX_THREADS = 512;
 
+// End of a 64-row tile computed by eight waves, wave w holding row group w % 4 (16 rows) of K
+// half w / 4 for 16 BH batch rows (acc[hb]: lane l has tile row 16 (w % 4) + l % 16 and batch
+// rows 16 hb + 4 (l / 16) + v). The two halves are added in a fixed order (half 0 + half 1)
+// through `red` (2 x 16 BH x 64 floats of free LDS), then the logits are stored and the
+// tile's (max, lowest index) candidate per batch row goes to the workspace, row-major
+// [batch row][tile].
+template <int BH>
+__device__ __forceinline__ void lm_tile64_finish(const LmHeadProblem& p, const f32x4_t (&acc)[BH], float* red,
+                                                 int n_tiles, int b0, int nbatch) {
+  constexpr int BROWS = 16 * BH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = wave & 3, hk = wave >> 2, r16 = lane & 15, q = lane >> 4;
+  const int tile = blockIdx.x, row0 = tile * LMX_ROWS, V = p.V;
+  static_for<BH>([&](auto hb) {
+    static_for<4>([&](auto v) {
+      constexpr int vv = v;
+      const int b = hb * 16 + q * 4 + vv;
+      red[(hk * BROWS + b) * LMX_ROWS + g * 16 + r16] = acc[hb][vv];
+    });
+  });
+  __syncthreads();
+  float* part_v = reinterpret_cast<float*>(p.workspace);
+  int* part_i = reinterpret_cast<int*>(part_v + (size_t)n_tiles * BROWS);
+  const int r = lane;  // row of the tile; each wave takes batch rows wave, wave + 8, ...
+  const bool ok_r = row0 + r < V;
+#pragma unroll
+  for (int b = wave; b < BROWS; b += LMX_THREADS / 64) {
+    const float sum = red[b * LMX_ROWS + r] + red[(BROWS + b) * LMX_ROWS + r];
+    if (ok_r && b < nbatch) p.logits[(int64_t)(b0 + b) * V + row0 + r] = sum;
+    float val = (ok_r && !(sum != sum)) ? sum : -INFINITY;
+    int idx = row0 + r;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(val, off, 64);
+      const int oi = __shfl_xor(idx, off, 64);
+      if (better(ov, oi, val, idx)) {
+        val = ov;
+        idx = oi;
+      }
+    }
+    if (lane == 0) {
+      part_v[(size_t)b * n_tiles + tile] = val;
+      part_i[(size_t)b * n_tiles + tile] = idx;
+    }
+  }
+}
+
 template <bool FP8, int BH>
 __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem p, int n_tiles, int b0) {
   using SH = LmxShape<BH>;
@@ -732,42 +783,223 @@ __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem
     __syncthreads();
   }
 
-  // The two K halves of each row group, added in order through LDS (the x buffers are free:
-  // every wave passed the loop's last barrier), then the logits and this workgroup's
-  // (max, lowest index) candidate per batch row.
-  float* red = reinterpret_cast<float*>(xs);  // [2][BROWS][64]
-  static_for<BH>([&](auto hb) {
+  // every wave passed the loop's last barrier: the x buffers are free for the reduction
+  lm_tile64_finish<BH>(p, acc, reinterpret_cast<float*>(xs), n_tiles, b0, nbatch);
+}
+
+// ---------------------------------------------------------------------------------------
+// Row-quad kernel (the default). The work split is the x-resident
+// kernel's: a workgroup owns 64 weight rows over the whole K, wave w multiplies row group
+// g = w % 4 (16 rows) over K half h = w / 4 of every x slice, x sits in LDS one slice of XS_K
+// columns at a time (double-buffered), and the weight goes to registers with non-temporal
+// 16-byte loads. What differs is the fetch shape. The operand layout wants 16 rows x 64
+// bytes per load instruction, and that shape streamed about 25% slower on this GPU than
+// 4 rows x 256 contiguous bytes, the fastest of the shapes measured (the same as a linear
+// sweep of the workgroup's rows). So here lane l of a load reads row l / 16 at bytes
+// 16 (l % 16) of a 256-byte run, and a "window" is four such loads: 16 rows x 256 bytes
+// (128 bf16 or 256 E4M3 K values). The wave writes its window to its own 4 KB of LDS and
+// reads it back in the operand layout (lane l: row l % 16, 16 bytes at chunk 4 t + l / 16 for
+// step t). No other wave touches that memory and a wave's LDS operations complete in
+// order, so the round trip needs no barrier.
+//
+// D windows of weight loads are in flight. A slice's x loads are issued just before the
+// weight loads of the slice's first window, so that waiting for them (before they are
+// written to LDS at the end of the previous slice) never waits for a weight load that is
+// not needed yet; two register sets hold them, which bounds D by twice the windows per
+// slice. Slices are visited from slice (tile mod slice count) on, wrapping, so that the
+// tiles in flight read different offsets of their rows (as in the LDS-ring kernel).
+//
+// Operand layout for v_mfma_f32_16x16x32_bf16 is the x-resident kernel's: x the row operand,
+// the weight the column operand; bf16 step t of a window takes K values 32 t + 8 q .. +8
+// (q = lane / 16); an E4M3 16-byte read covers K values 64 t + 16 q .. +16, the first eight
+// feeding one MFMA and the rest the next (the same permutation of K applied to x).
+constexpr int lm_gcd(int a, int b) { return b == 0 ? a : lm_gcd(b, a % b); }
+constexpr int lm_lcm(int a, int b) { return a / lm_gcd(a, b) * b; }
+
+template <bool FP8, int XS_K, int BH>
+struct LmqShape {
+  static constexpr int BROWS = 16 * BH;              // batch rows per pass: 32 or 64
+  static constexpr int WIN_K = FP8 ? 256 : 128;      // K values per window (256 bytes of a row)
+  static constexpr int WPS = XS_K / 2 / WIN_K;       // windows per slice per wave
+  static constexpr int XBYTES = BROWS * XS_K * 2;    // one x buffer
+  static constexpr int XCH = XBYTES / 16 / 512;      // 16-byte x chunks per thread per slice
+  static constexpr int STAGE = 16 * 256;             // one wave's window in LDS
+  static constexpr int LDS = 2 * XBYTES + 8 * STAGE;
+  static_assert(WPS >= 1 && XCH >= 1 && LDS <= 160 * 1024, "row-quad shape");
+};
+
+template <bool FP8, int XS_K, int D, int NXS, bool ROT, int BH>
+__global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int n_tiles, int b0) {
+  using SH = LmqShape<FP8, XS_K, BH>;
+  constexpr int WIN_K = SH::WIN_K, WPS = SH::WPS, XROW = XS_K * 2, XCH = SH::XCH;
+  static_assert(D >= 1 && D <= NXS * WPS, "NXS x register sets allow D <= NXS windows per slice");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::LDS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = p.K, V = p.V;
+  const int nbatch = min(SH::BROWS, p.B - b0);
+  const int tile = blockIdx.x, row0 = tile * 64;
+  const int g = wave & 3, hk = wave >> 2;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int nslice = K / XS_K, nw = nslice * WPS;
+  const int rot = ROT ? tile % nslice : 0;
+  const int nkb = K / 128;
+  unsigned char* const xs = lds;                                  // [2][BROWS][XS_K] bf16
+  unsigned char* const stage = lds + 2 * SH::XBYTES + wave * SH::STAGE;
+
+  // Load layout: lane l of quad j reads row 16 g + 4 j + l / 16 (a row past V reads row V - 1;
+  // its outputs are never stored) at bytes 16 (l % 16) of the window.
+  const unsigned char* wq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = min(row0 + 16 * g + 4 * j + q, V - 1);
+    wq[j] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)row * (FP8 ? K : 2 * K) + 16 * r16;
+  }
+  // Operand layout: lane l holds row 16 g + l % 16.
+  const int myrow = row0 + 16 * g + r16;
+  const bool rok = myrow < V;
+  const float* srow = FP8 ? p.wscale + (int64_t)min(myrow, V - 1) * nkb : nullptr;
+
+  auto slice_of = [&](int si) { return si + rot < nslice ? si + rot : si + rot - nslice; };
+  // first K value of this wave's window wi
+  auto win_k = [&](int wi) { return slice_of(wi / WPS) * XS_K + hk * (XS_K / 2) + (wi % WPS) * WIN_K; };
+
+  struct Win {
+    u32x4_t w[4];
+    float sc[2];
+  };
+  auto wload = [&](int wi, Win& r) {
+    const int k = win_k(wi);
+    const int64_t off = FP8 ? (int64_t)k : 2 * (int64_t)k;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wq[j] + off));
+    if constexpr (FP8) {
+      r.sc[0] = srow[k / 128];
+      r.sc[1] = srow[k / 128 + 1];
+    }
+  };
+  // x slice si (in visiting order): thread chunk j is chunk tid + 512 j of the [BROWS][XS_K]
+  // slice; batch rows past the pass read row b0 (their outputs are never stored). Row b's
+  // chunk c sits at chunk c ^ (b % 16).
+  u32x4_t xr[NXS][XCH];  // register sets, by slice index mod NXS
+  auto xload = [&](int si, u32x4_t (&d)[XCH]) {
+    const int s = slice_of(si);
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+      const int id = tid + 512 * j, b = id / (XS_K / 8), c = id % (XS_K / 8);
+      d[j] = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(b0 + (b < nbatch ? b : 0)) * K + s * XS_K + c * 8);
+    }
+  };
+  auto xstore = [&](int buf, const u32x4_t (&d)[XCH]) {
+    unsigned char* base = xs + buf * SH::XBYTES;
+#pragma unroll
+    for (int j = 0; j < XCH; ++j) {
+      const int id = tid + 512 * j, b = id / (XS_K / 8), c = id % (XS_K / 8);
+      *reinterpret_cast<u32x4_t*>(base + b * XROW + ((c ^ (b & 15)) << 4)) = d[j];
+    }
+  };
+
+  f32x4_t acc[BH], part[BH];
+  static_for<BH>([&](auto h) {
     static_for<4>([&](auto v) {
-      constexpr int vv = v;
-      const int b = hb * 16 + q * 4 + vv;
-      red[(hk * BROWS + b) * LMX_ROWS + g * 16 + r16] = acc[hb][vv];
+      acc[h][decltype(v)::value] = 0.0f;
+      part[h][decltype(v)::value] = 0.0f;
     });
   });
-  __syncthreads();
-  float* part_v = reinterpret_cast<float*>(p.workspace);
-  int* part_i = reinterpret_cast<int*>(part_v + (size_t)n_tiles * BROWS);
-  const int r = lane;  // row of the tile; each wave takes batch rows wave, wave + 8, ...
-  const bool ok_r = row0 + r < V;
+
+  auto compute = [&](const Win& r, int buf, int w2) {
+    // the window through this wave's LDS stage: row R's chunk C at chunk C ^ R
 #pragma unroll
-  for (int b = wave; b < BROWS; b += LMX_THREADS / 64) {
-    const float sum = red[b * LMX_ROWS + r] + red[(BROWS + b) * LMX_ROWS + r];
-    if (ok_r && b < nbatch) p.logits[(int64_t)(b0 + b) * V + row0 + r] = sum;
-    float val = (ok_r && !(sum != sum)) ? sum : -INFINITY;
-    int idx = row0 + r;
+    for (int j = 0; j < 4; ++j) {
+      const int row = 4 * j + q;
+      *reinterpret_cast<u32x4_t*>(stage + row * 256 + ((r16 ^ row) << 4)) = r.w[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    u32x4_t wf[4];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(val, off, 64);
-      const int oi = __shfl_xor(idx, off, 64);
-      if (better(ov, oi, val, idx)) {
-        val = ov;
-        idx = oi;
+    for (int t = 0; t < 4; ++t)
+      wf[t] = *reinterpret_cast<const u32x4_t*>(stage + r16 * 256 + (((4 * t + q) ^ r16) << 4));
+    const unsigned char* xb = xs + buf * SH::XBYTES;
+    const int cx0 = hk * (XS_K / 16) + w2 * (WIN_K / 8);  // the window's first x chunk
+    auto xfrag = [&](int hb, int c) {
+      return __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(xb + (hb * 16 + r16) * XROW + ((c ^ r16) << 4)));
+    };
+    static_for<4>([&](auto tt) {
+      constexpr int t = tt;
+      if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t lo = h ? wf[t][2] : wf[t][0], hi = h ? wf[t][3] : wf[t][1];
+          u32x4_t wv;
+          wv[0] = e4m3x2_to_bf16x2<false>(lo);
+          wv[1] = e4m3x2_to_bf16x2<true>(lo);
+          wv[2] = e4m3x2_to_bf16x2<false>(hi);
+          wv[3] = e4m3x2_to_bf16x2<true>(hi);
+          const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wv);
+          const int c = cx0 + 8 * t + 2 * q + h;
+          static_for<BH>([&](auto hb) {
+            part[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xfrag(hb, c), wb, part[hb], 0, 0, 0);
+          });
+        }
+        if constexpr (t % 2 == 1) {  // a 128-wide block is complete: scale it into the sum
+          const float sc = rok ? r.sc[t / 2] : 0.0f;
+          static_for<BH>([&](auto hb) {
+            static_for<4>([&](auto v) {
+              constexpr int vv = v;
+              acc[hb][vv] = fmaf(part[hb][vv], sc, acc[hb][vv]);
+              part[hb][vv] = 0.0f;
+            });
+          });
+        }
+      } else {
+        const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wf[t]);
+        const int c = cx0 + 4 * t + q;
+        static_for<BH>([&](auto hb) {
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xfrag(hb, c), wb, acc[hb], 0, 0, 0);
+        });
       }
-    }
-    if (lane == 0) {
-      part_v[(size_t)b * n_tiles + tile] = val;
-      part_i[(size_t)b * n_tiles + tile] = idx;
-    }
-  }
+    });
+  };
+
+  // The window loop runs in periods of PER windows, a common multiple of D and of two slices,
+  // so that every ring slot, x register set and x buffer index is a constant and every load
+  // is unconditional: the wait before each use then counts exactly the loads issued after it.
+  // The last period issues no loads past the last window.
+  constexpr int PER = lm_lcm(lm_lcm(D, NXS * WPS), 2 * WPS);
+  Win ring[D];
+  xload(0, xr[0]);
+  static_for<D>([&](auto jj) {
+    constexpr int j = jj;
+    if constexpr (j > 0 && j % WPS == 0) xload(j / WPS, xr[(j / WPS) % NXS]);
+    wload(j, ring[j]);
+  });
+  xstore(0, xr[0]);
+  __syncthreads();
+  auto period = [&](int base, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
+    static_for<PER>([&](auto jj) {
+      constexpr int j = jj;
+      constexpr int slot = j % D, w2 = j % WPS, par = (j / WPS) & 1;
+      compute(ring[slot], par, w2);
+      constexpr int nxj = j + D;  // the window whose loads take this slot
+      if constexpr (!LAST || nxj < PER) {
+        if constexpr (nxj % WPS == 0) xload((base + nxj) / WPS, xr[(nxj / WPS) % NXS]);
+        wload(base + nxj, ring[slot]);
+      }
+      if constexpr (w2 == WPS - 1) {  // a slice is done: the next one to LDS
+        if constexpr (!LAST || j != PER - 1) xstore(par ^ 1, xr[(j / WPS + 1) % NXS]);
+        __syncthreads();
+      }
+    });
+  };
+  int base = 0;
+  for (; base < nw - PER; base += PER) period(base, std::false_type{});
+  period(base, std::true_type{});
+  // the last window ended a slice: every wave passed that barrier, the x buffers are free
+  lm_tile64_finish<BH>(p, acc, reinterpret_cast<float*>(xs), n_tiles, b0, nbatch);
 }
 
 // Reduces every workgroup's (max, lowest index) candidate of one batch row (one workgroup
@@ -914,10 +1146,52 @@ void launch_xres(const LmHeadProblem& p, int b0, hipStream_t stream) {
 bool xres_ok(const LmHeadProblem& p) { return p.w_fp8 ? p.K % 128 == 0 : p.K % 32 == 0; }
 int xres_pass_rows(const LmHeadProblem& p) { return p.B <= 32 ? 32 : 64; }
 
-// The default launch shape: the LDS ring up to 32 batch rows; for more, the x-resident kernel,
-// which streams the weight once per 64 rows instead of once per 32 (measured on the decode
-// workload, K 4096, 16032 rows: 64 rows 44.8 against 63.5 us bf16, 36.9 against 52.4 us E4M3).
-int default_shape(const LmHeadProblem& p) { return p.B > 32 && xres_ok(p) ? kLmXresShape : kLmDefaultShape; }
+// Row-quad kernel. Shapes kLmQuadShape + i take variant i: x slice width, windows in flight,
+// x register sets, staggered slice order, 16-row batch groups per pass; for bf16 and E4M3.
+struct LmQuadCfg {
+  int xs_k, d, nxs, rot, bh;
+};
+constexpr int kLmQuadCount = 5;
+constexpr LmQuadCfg kLmQuad[kLmQuadCount][2] = {
+    {{256, 2, 2, 1, 2}, {1024, 2, 2, 1, 2}},  // the default up to 32 batch rows
+    {{256, 2, 2, 1, 4}, {512, 2, 2, 1, 4}},   // the default above: 64-row passes
+    {{256, 4, 4, 1, 2}, {512, 4, 4, 1, 2}},   {{512, 4, 2, 1, 2}, {512, 2, 2, 1, 2}},
+    {{512, 2, 2, 1, 4}, {512, 1, 1, 1, 4}}};
+bool is_quad(int shape) { return shape >= kLmQuadShape && shape < kLmQuadShape + kLmQuadCount; }
+int quad_pass_rows(const LmHeadProblem& p, int shape) { return 16 * kLmQuad[shape - kLmQuadShape][p.w_fp8 ? 1 : 0].bh; }
+// K must hold whole periods of windows (see lm_head_quad_kernel).
+bool quad_ok(const LmHeadProblem& p, int shape) {
+  const int fp8 = p.w_fp8 ? 1 : 0;
+  const LmQuadCfg& c = kLmQuad[shape - kLmQuadShape][fp8];
+  const int wps = c.xs_k / 2 / (fp8 ? 256 : 128);
+  return p.K >= c.xs_k && p.K % c.xs_k == 0 && (p.K / c.xs_k * wps) % lm_lcm(lm_lcm(c.d, c.nxs * wps), 2 * wps) == 0;
+}
+template <bool FP8, int I>
+void launch_quad(const LmHeadProblem& p, int b0, hipStream_t stream) {
+  constexpr LmQuadCfg c = kLmQuad[I][FP8];
+  const int n_tiles = (p.V + 63) / 64;
+  hipLaunchKernelGGL((lm_head_quad_kernel<FP8, c.xs_k, c.d, c.nxs, c.rot != 0, c.bh>), dim3(n_tiles), dim3(512), 0,
+                     stream, p, n_tiles, b0);
+  hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(min(16 * c.bh, p.B - b0)), dim3(LM_FIN_THREADS), 0, stream, p, n_tiles,
+                     b0, 16 * c.bh);
+}
+
+// A row-quad shape whose slice width does not divide K runs the LDS-ring default instead.
+int effective_shape(const LmHeadProblem& p, int shape) {
+  if (is_quad(shape) && !quad_ok(p, shape)) return kLmRingShape;
+  return shape;
+}
+
+// The default launch shape: the row-quad kernel, in 32-row batch passes up to 32 rows and in
+// 64-row passes above, which stream the weight once per 64 rows. On the decode workload (K 4096,
+// 16032 rows; kernel times from a HIP kernel trace): 32 rows 25.1 us bf16 and 20.2 us E4M3,
+// against 30.3 and 24.3 us for the LDS ring; 64 rows in one pass 30.8 and 28.9 us, against
+// 40.2 and 32.7 us for the x-resident kernel. A K that the row-quad kernel cannot take runs the
+// x-resident kernel above 32 rows if it can, else the LDS ring.
+int default_shape(const LmHeadProblem& p) {
+  if (p.B > 32) return quad_ok(p, kLmQuadShape + 1) ? kLmQuadShape + 1 : xres_ok(p) ? kLmXresShape : kLmRingShape;
+  return quad_ok(p, kLmQuadShape) ? kLmQuadShape : kLmRingShape;
+}
 
 template <bool FP8>
 void launch_any(const LmHeadProblem& p, int shape, int b0, hipStream_t stream) {
@@ -936,6 +1210,11 @@ void launch_any(const LmHeadProblem& p, int shape, int b0, hipStream_t stream) {
       if (xres_pass_rows(p) == 32) launch_xres<FP8, 2>(p, b0, stream);
       else launch_xres<FP8, 4>(p, b0, stream);
       break;
+    case kLmQuadShape: launch_quad<FP8, 0>(p, b0, stream); break;
+    case kLmQuadShape + 1: launch_quad<FP8, 1>(p, b0, stream); break;
+    case kLmQuadShape + 2: launch_quad<FP8, 2>(p, b0, stream); break;
+    case kLmQuadShape + 3: launch_quad<FP8, 3>(p, b0, stream); break;
+    case kLmQuadShape + 4: launch_quad<FP8, 4>(p, b0, stream); break;
     case 1: launch_shape<FP8, 1>(p, b0, stream); break;
     case 2: launch_shape<FP8, 2>(p, b0, stream); break;
     case 3: launch_shape<FP8, 3>(p, b0, stream); break;
@@ -949,7 +1228,7 @@ void launch_any(const LmHeadProblem& p, int shape, int b0, hipStream_t stream) {
 
 }  // namespace
 
-int lm_head_shape_count() { return (int)(sizeof(kLmShapes) / sizeof(kLmShapes[0])) + 3; }
+int lm_head_shape_count() { return kLmQuadShape + kLmQuadCount; }
 
 // Workspace of one launch shape (-1: the default): per-workgroup candidates, or KS slices of
 // partial logits for one batch pass.
@@ -959,6 +1238,9 @@ size_t lm_head_shape_workspace_bytes(int shape, int B, int V, int K, bool fp8, i
   q.K = K;
   q.w_fp8 = fp8;
   if (shape < 0) shape = default_shape(q);
+  shape = effective_shape(q, shape);
+  if (is_quad(shape))
+    return (size_t)((V + 63) / 64) * quad_pass_rows(q, shape) * (sizeof(float) + sizeof(int));
   if (shape == kLmXresShape && xres_ok(q))
     return (size_t)((V + LMX_ROWS - 1) / LMX_ROWS) * xres_pass_rows(q) * (sizeof(float) + sizeof(int));
   if (shape == kLmDmaShape || shape == kLmDmaShape + 1)
@@ -1021,8 +1303,9 @@ hipError_t lm_head_scratch(void** ptr, size_t* bytes) {
 hipError_t launch_lm_head(const LmHeadProblem& p, int shape, hipStream_t stream) {
   if (shape < 0) shape = default_shape(p);
   if (shape >= lm_head_shape_count()) return hipErrorInvalidValue;
+  shape = effective_shape(p, shape);
   if (shape == kLmXresShape && !xres_ok(p)) shape = 4;  // ragged K: the register-streaming kernel
-  const int pass = shape == kLmXresShape ? xres_pass_rows(p) : LM_BATCH;
+  const int pass = shape == kLmXresShape ? xres_pass_rows(p) : is_quad(shape) ? quad_pass_rows(p, shape) : LM_BATCH;
   for (int b0 = 0; b0 < p.B; b0 += pass) {
     if (p.w_fp8)
       launch_any<true>(p, shape, b0, stream);

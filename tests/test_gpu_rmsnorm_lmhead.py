@@ -183,3 +183,23 @@ def test_lm_head_x_resident_slices_and_batch_passes(fp8, B, K, vocab):
         assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])
     finally:
         tt.set_lm_head_shape(-1)
+
+
+@pytest.mark.parametrize("shape", [11, 12, 13, 14, 15])
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("B,K,vocab,tp", [(32, 2048, 8013, 8), (7, 4096, 201, 2), (40, 2048, 258, 2),
+                                          (70, 4096, 8013, 8)])
+def test_lm_head_row_quad_kernel(shape, fp8, B, K, vocab, tp):
+    """The row-quad kernel at each of its slice widths, load depths and batch pass sizes (32 or
+    64 rows): a full 32-row pass over a 1002-row shard (its last 64-row tile partial), a short
+    batch over K 4096 (several periods of windows), 40 rows (two 32-row passes or one short
+    64-row pass) over a 129-row shard (three tiles, the last holding one row), and 70 rows
+    (three or two passes)."""
+    tt.set_lm_head_shape(shape)
+    try:
+        lg, idx, mx, ref = _lm_case(B, K, vocab, tp, 1, 500, 130 + shape, fp8)
+        assert argmax_ok(idx.cpu().numpy(), ref) == []
+        i = idx.cpu().numpy()
+        assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])
+    finally:
+        tt.set_lm_head_shape(-1)
