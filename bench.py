@@ -285,7 +285,8 @@ def cpu_baseline(budget_s: float):
     rows4 = done * rows_per_block
     fl4 = 2.0 * rows4 * w.shape[0] * c["hidden"]
     full4 = 2.0 * x.shape[0] * w.shape[0] * c["hidden"]
-    per.append((4, fl4, dt4, f"{rows4} of the 32768 rows in 256-row blocks"))
+    per.append((4, fl4, dt4, f"{rows4} rows: the 32768 rows' 256-row blocks in order, repeated past the last "
+                             f"for the time budget"))
     per.sort()
     entries = [{"workload": k, "gflop": round(fl / 1e9, 3), "seconds": round(t, 3),
                 "tflops": round(fl / t / 1e12, 4), "sample": smp} for k, fl, t, smp in per]
@@ -294,7 +295,7 @@ def cpu_baseline(budget_s: float):
     step_fl = sum(fl for k, fl, t, _ in per if k != 4) + full4
     return {
         "value": step_fl / step_s / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"numpy float64 oracle on workloads 1-3 in full and {rows4} rows of workload 4 "
+        "sample": f"numpy float64 oracle on workloads 1-3 and 5 in full and {rows4} rows of workload 4 "
                   f"(the step's GEMM flops over its time, workload 4 scaled to 32768 rows: {step_s:.1f} s per step); "
                   f"{sum(t for _, _, t, _ in per) + sum(e['seconds'] for e in lm):.1f} s of oracle time "
                   f"({time.perf_counter() - t_all:.1f} s with input generation); {os.cpu_count()} host cpus, "

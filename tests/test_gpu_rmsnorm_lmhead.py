@@ -203,3 +203,67 @@ def test_lm_head_row_quad_kernel(shape, fp8, B, K, vocab, tp):
         assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])
     finally:
         tt.set_lm_head_shape(-1)
+
+
+@pytest.mark.parametrize("shape", [-1, 0, 9, 10, 11, 12])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_lm_head_special_values(shape, fp8):
+    """NaN and infinite inputs through every kernel family: a NaN weight row, a NaN batch row, an
+    infinite x entry whose weight column holds zeros (inf * 0 = NaN), negative and positive
+    values, and (bf16) infinite weights tied at two rows. The expected logits are the oracle's
+    sums over the finite entries plus the non-finite products in IEEE arithmetic; the argmax
+    ignores NaN, takes the lowest index among equal maxima, and gives index 0 (maximum -inf) to
+    a row of NaN logits."""
+    B, K, V = 4, 2048, 300
+    x = synth.bf16_integers((B, K), -2, 2, 41)
+    x[0, 5], x[1, 5], x[2, 5] = 0x7F80, 0, 0                 # +inf in batch row 0, column 5
+    x[:3, 1] = synth.bf16_from_float(np.array([1.0, -1.0, 0.0]))
+    x[3, :] = 0x7FC0                                         # a NaN batch row
+    if fp8:
+        g = np.random.default_rng(42)
+        q = g.choice(np.array([0x30, 0x38, 0x3C, 0xB0, 0xB8, 0x00], dtype=np.uint8), size=(V, K))
+        q[:, 5] = 0x38                                       # +1: row v gets +inf in batch row 0 ...
+        q[:5, 5] = 0x00                                      # ... except rows 0-4 (inf * 0 = NaN)
+        q[40, 5] = 0xB8                                      # -1: -inf
+        q[10, 0] = 0x7F                                      # a NaN weight row
+        s = (2.0 ** g.integers(-2, 3, size=(V, K // 128))).astype(np.float32)
+        wd = oracle.e4m3_to_f64(q) * np.repeat(s.astype(np.float64), 128, axis=1)
+        qf = q.copy()
+        qf[10, 0] = 0
+        finite = oracle.lm_head_sums(np.where(np.isfinite(oracle.bf16_to_f64(x)), x, 0).astype(np.uint16),
+                                     w_fp8=qf, w_scale=s)
+        W, dt, S = dev_u8(q), tt.TP_DTYPE_FP8_E4M3, dev_f32(s)
+    else:
+        w = synth.bf16_integers((V, K), -2, 2, 43)
+        w[:, 5] = synth.bf16_from_float(np.ones(V))
+        w[:5, 5] = 0
+        w[40, 5] = synth.bf16_from_float(np.array([-1.0]))[0]
+        w[10, 0] = 0x7FC0                                    # a NaN weight row
+        w[[20, 250], 1] = 0x7F80                             # +inf: batch row 0 +inf (already), row 1 -inf, row 2 NaN
+        w[100, 2] = 0xFF80                                   # -inf
+        wd = oracle.bf16_to_f64(w)
+        wf = np.where(np.isfinite(wd), w, 0).astype(np.uint16)
+        finite = oracle.lm_head_sums(np.where(np.isfinite(oracle.bf16_to_f64(x)), x, 0).astype(np.uint16), wf)
+        W, dt, S = dev_bf16(w), tt.TP_DTYPE_BF16, None
+    xd = oracle.bf16_to_f64(x)
+    ref = finite.copy()
+    with np.errstate(invalid="ignore"):
+        for b in range(B):
+            for k in np.nonzero(~np.isfinite(xd[b]) | ~np.isfinite(wd).all(axis=0))[0]:
+                special = ~np.isfinite(xd[b, k]) | ~np.isfinite(wd[:, k])
+                ref[b, special] = ref[b, special] + xd[b, k] * wd[special, k]
+    ref = oracle.f32(ref)
+    if shape >= 0:
+        tt.set_lm_head_shape(shape)
+    try:
+        lg, idx, mx = tt.lm_head_shard_argmax(dev_bf16(x), V, 1, 0, 128, W, dt, S)
+    finally:
+        tt.set_lm_head_shape(-1)
+    got = host_f32(lg)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])                  # integer sums and infinities: exact
+    ref_i, ref_m = oracle.shard_argmax(ref)
+    assert np.array_equal(idx.cpu().numpy(), ref_i)
+    assert np.array_equal(host_f32(mx), ref_m)
+    assert ref_i[3] == 0 and ref_m[3] == -np.inf and ref_m[0] == np.inf
