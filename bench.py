@@ -132,7 +132,7 @@ class Workloads:
             self.lg5 = torch.empty((B, V_r), dtype=torch.float32, device=dev)
             self.am5 = torch.empty((B,), dtype=torch.int32, device=dev)
             self.mx5 = torch.empty((B,), dtype=torch.float32, device=dev)
-            self.ws5 = tt.lm_head_workspace(B, c["vocab"], c["tp"], c["rank"], c["chunk"], dev)
+            self.ws5 = tt.lm_head_workspace(B, c["vocab"], c["tp"], c["rank"], dev)
             K = c["hidden"]
             self.bytes5 = {
                 "bf16": V_r * K * 2 + B * K * 2 + B * V_r * 4,

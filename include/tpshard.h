@@ -301,10 +301,12 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
                           size_t workspace_bytes, void* stream);
 
 /*
- * tp_lm_head_workspace_bytes - device workspace lm_head_shard_argmax needs (enough for any
- * batch size up to B and any of the library's launch shapes; 0 for invalid arguments).
+ * tp_lm_head_workspace_bytes - device workspace lm_head_shard_argmax needs: enough for any
+ * batch size, any max_rows_per_chunk and any of the library's launch shapes (256 bytes per
+ * row of the rank's vocab shard). B, vocab, tp_size and rank are checked as in
+ * lm_head_shard_argmax; 0 for invalid arguments.
  */
-TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk);
+TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank);
 
 /*
  * lm_head_shard_argmax - a vocab shard's float32 logits and per-row argmax (decode).

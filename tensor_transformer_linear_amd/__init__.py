@@ -53,7 +53,7 @@ SIGNATURES = {
     "tp_rmsnorm_workspace_min_bytes": (_sz, [_i64, _i64]),
     "rmsnorm_column_linear": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp, _P64, _int, _int, _int,
                                      _vp, _int, _int, _i64, _vp, _sz, _vp]),
-    "tp_lm_head_workspace_bytes": (_sz, [_i64, _i64, _int, _int, _i64]),
+    "tp_lm_head_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
     "lm_head_shard_argmax": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _int, _vp, _vp, _vp, _vp, _vp,
                                     _sz, _vp]),
     "lm_head_shard_argmax_noalloc": (_int, [_vp, _i64, _i64, _i64, _int, _int, _i64, _vp, _int, _vp, _vp, _vp, _vp,
@@ -471,13 +471,13 @@ def rmsnorm_column_linear(x, scale, eps, w_shard, bias_shard, subparam_sizes, tp
     return y
 
 
-def tp_lm_head_workspace_bytes(B, vocab, tp_size, rank, max_rows_per_chunk) -> int:
-    return int(lib().tp_lm_head_workspace_bytes(B, vocab, tp_size, rank, max_rows_per_chunk))
+def tp_lm_head_workspace_bytes(B, vocab, tp_size, rank) -> int:
+    return int(lib().tp_lm_head_workspace_bytes(B, vocab, tp_size, rank))
 
 
-def lm_head_workspace(B, vocab, tp_size, rank, max_rows_per_chunk, device="cuda"):
+def lm_head_workspace(B, vocab, tp_size, rank, device="cuda"):
     """A workspace for ``lm_head_shard_argmax`` (scratch; zeroed here only for tidiness)."""
-    n = tp_lm_head_workspace_bytes(B, vocab, tp_size, rank, max_rows_per_chunk)
+    n = tp_lm_head_workspace_bytes(B, vocab, tp_size, rank)
     if n == 0:
         raise TpError(TP_ERR_INVALID_ARG, "invalid LM-head workspace query")
     return torch.zeros(n, dtype=torch.uint8, device=device)
@@ -508,7 +508,7 @@ def lm_head_shard_argmax(x, vocab, tp_size, rank, max_rows_per_chunk, w_shard, w
     if max_logit is None:
         max_logit = torch.empty((B,), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = lm_head_workspace(B, vocab, tp_size, rank, max_rows_per_chunk, dev)
+        workspace = lm_head_workspace(B, vocab, tp_size, rank, dev)
     _call("lm_head_shard_argmax", _ptr(x), B, K, vocab, tp_size, rank, max_rows_per_chunk, _ptr(w_shard), w_dtype,
           _ptr(w_block_scale), _ptr(logits), _ptr(argmax_local), _ptr(max_logit), _ptr(workspace),
           workspace.numel(), _stream(stream))

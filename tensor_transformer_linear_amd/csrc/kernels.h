@@ -113,7 +113,7 @@ struct LmHeadProblem {
   float* maxval;         // f32 [B] or nullptr
   void* workspace;
 };
-size_t lm_head_workspace_bytes(int B, int V, int chunk);  // the largest need over the launch shapes
+size_t lm_head_workspace_bytes(int V);  // the largest need over the launch shapes and chunk sizes
 // The workspace one launch shape needs (-1: the default shape).
 size_t lm_head_shape_workspace_bytes(int shape, int B, int V, int K, bool fp8, int chunk);
 // This GPU's device scratch for the allocation-free entry point (its address, found once per

@@ -1253,18 +1253,14 @@ size_t lm_head_shape_workspace_bytes(int shape, int B, int V, int K, bool fp8, i
   return max(cand, slices);
 }
 
-size_t lm_head_workspace_bytes(int B, int V, int chunk) {
-  (void)B;
-  // the largest need over the launch shapes: per-workgroup candidates, or KS slices of
-  // partial logits for one 32-row batch pass
-  size_t need = 0;
-  int per;
-  for (const LmShape& sh : kLmShapes) {
-    const size_t cand = (size_t)lm_tiles(V, chunk, sh.G * 16, &per) * LM_BATCH * (sizeof(float) + sizeof(int));
-    const size_t slices = sh.KS > 1 ? (size_t)sh.KS * LM_BATCH * V * sizeof(float) : 0;
-    need = max(need, max(cand, slices));
-  }
-  // the x-resident kernel: candidates of up to 64 batch rows per 64-row tile
+size_t lm_head_workspace_bytes(int V) {
+  // The largest need over the launch shapes and every chunk size: per-workgroup candidates
+  // (the register-streaming shapes tile each chunk, so one-row chunks give V tiles), KS slices
+  // of partial logits for one 32-row batch pass, or the 64-row kernels' candidates of up to 64
+  // batch rows per 64-row tile.
+  size_t need = (size_t)V * LM_BATCH * (sizeof(float) + sizeof(int));
+  for (const LmShape& sh : kLmShapes)
+    if (sh.KS > 1) need = max(need, (size_t)sh.KS * LM_BATCH * V * sizeof(float));
   need = max(need, (size_t)((V + LMX_ROWS - 1) / LMX_ROWS) * 64 * (sizeof(float) + sizeof(int)));
   return need;
 }

@@ -572,13 +572,9 @@ TP_API int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void
                                       tpabi::Tuning{});
 }
 
-TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank, int64_t max_rows_per_chunk) {
-  if (B < 1 || vocab < 1 || tp_size < 1 || rank < 0 || rank >= tp_size || max_rows_per_chunk < 1 || vocab < tp_size ||
-      vocab > INT_MAX)
-    return 0;
-  const int64_t V_r = width_of(vocab, tp_size, rank);
-  const int64_t chunk = max_rows_per_chunk < V_r ? max_rows_per_chunk : V_r;
-  return tpk::lm_head_workspace_bytes((int)B, (int)V_r, (int)chunk);
+TP_API size_t tp_lm_head_workspace_bytes(int64_t B, int64_t vocab, int tp_size, int rank) {
+  if (B < 1 || vocab < 1 || tp_size < 1 || rank < 0 || rank >= tp_size || vocab < tp_size || vocab > INT_MAX) return 0;
+  return tpk::lm_head_workspace_bytes((int)width_of(vocab, tp_size, rank));
 }
 
 TP_API int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,

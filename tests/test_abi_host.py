@@ -195,10 +195,11 @@ def test_lm_head_rejects(kw, status):
 
 
 def test_lm_head_workspace_query():
-    n = tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0, 4008)
-    assert n > 0
-    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 8, 4008) == 0
-    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0, 0) == 0
+    # enough for every launch shape and chunk size: 256 bytes per shard row
+    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 0) == 16032 * 256
+    assert tt.tp_lm_head_workspace_bytes(100, 4001, 1, 0) == 4001 * 256
+    assert tt.tp_lm_head_workspace_bytes(32, 128256, 8, 8) == 0
+    assert tt.tp_lm_head_workspace_bytes(0, 128256, 8, 0) == 0
 
 
 def test_tuning_choices_checked_before_anything_else():

@@ -40,7 +40,7 @@ def test_graph_replays_match_eager():
     lg = torch.empty((B, V_r), dtype=torch.float32, device=dev)
     am = torch.empty((B,), dtype=torch.int32, device=dev)
     mx = torch.empty((B,), dtype=torch.float32, device=dev)
-    ws = tt.lm_head_workspace(B, vocab, 2, 1, chunk)
+    ws = tt.lm_head_workspace(B, vocab, 2, 1)
     yf = torch.zeros((M, h_r, qkv + fph), dtype=torch.bfloat16, device=dev)
     q = torch.empty((M, h_r, qkv), dtype=torch.bfloat16, device=dev)
     outs = g_out + [part, z, lg, am, mx, yf, q] + parts

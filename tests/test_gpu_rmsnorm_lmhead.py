@@ -114,7 +114,7 @@ def test_lm_head_planted_argmax_and_ties():
         w[pos, ks[b]] = synth.bf16_from_float(np.array([9.0]))[0]
     for pos in (100, 9000, 12000):
         w[pos, ks[6]] = synth.bf16_from_float(np.array([11.0]))[0]
-    ws = tt.lm_head_workspace(B, V, 1, 0, C)
+    ws = tt.lm_head_workspace(B, V, 1, 0)
     for _ in range(3):  # the workspace is reused across calls
         lg, idx, mx = tt.lm_head_shard_argmax(dev_bf16(x), V, 1, 0, C, dev_bf16(w), workspace=ws)
         got = idx.cpu().numpy()
