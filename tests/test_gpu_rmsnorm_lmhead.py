@@ -267,3 +267,17 @@ def test_lm_head_special_values(shape, fp8):
     assert np.array_equal(idx.cpu().numpy(), ref_i)
     assert np.array_equal(host_f32(mx), ref_m)
     assert ref_i[3] == 0 and ref_m[3] == -np.inf and ref_m[0] == np.inf
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("B,K,vocab,tp", [(1, 512, 40, 1), (33, 2048, 1000, 2), (64, 4096, 700, 1), (65, 2048, 300, 1),
+                                          (5, 1536, 300, 1)])
+def test_lm_head_default_shape_edges(fp8, B, K, vocab, tp):
+    """The default launch choice at its edges: one row over a shard shorter than one 64-row tile,
+    33 and 64 rows (one 64-row pass), 65 rows (a second pass of one row), the smallest K the
+    row-quad kernel takes (512 bf16; 2048 E4M3), and K 1536, which the E4M3 row-quad kernel does
+    not take (the LDS ring runs instead)."""
+    lg, idx, mx, ref = _lm_case(B, K, vocab, tp, 0, 64, 170 + B, fp8)
+    assert argmax_ok(idx.cpu().numpy(), ref) == []
+    i = idx.cpu().numpy()
+    assert np.array_equal(host_f32(mx), host_f32(lg)[np.arange(B), i])
