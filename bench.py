@@ -21,6 +21,7 @@ are on the device before timing starts.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -55,6 +56,13 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run device-to-device copies of MB megabytes (the known-size kernel that "
                          "calibrates the HBM byte counters) and exit")
+    ap.add_argument("--lm-shapes", default="", metavar="LIST",
+                    help="only run the decode LM head (workload 5 with 32 and 64 batch rows, bf16 and E4M3 "
+                         "weights) under each listed launch shape (keys of LM_HEAD_SHAPES, through the tuning "
+                         "library), 25 calls each, and exit; a kernel trace of this run gives the kernel times")
+    ap.add_argument("--stream-probe", type=int, default=0, metavar="N",
+                    help="only stream a bf16 LM-head weight shard (16032 rows x 8192 bytes, rotated copies) N "
+                         "times in each fetch shape of the tuning library's probe and exit")
     return ap.parse_args()
 
 
@@ -624,6 +632,91 @@ def gemm_launches(n: int) -> None:
     print(json.dumps({"gemm_launches": n, "segments": [l for l, _ in segs]}), flush=True)
 
 
+def lm_shapes(shapes) -> None:
+    """The decode LM head under each given launch shape: 32 and 64 batch rows, bf16 and E4M3
+    weights rotating over >= 512 MB of copies, 5 + 20 calls per setting, event-timed (the call
+    times include the host's launch work; the kernels' own times come from a kernel trace)."""
+    import torch
+
+    import synth
+    import tensor_transformer_linear_amd as tt
+
+    dev = torch.device("cuda:0")
+    c = synth.WORKLOADS[5]
+    inp = synth.workload_inputs(5)
+    w = torch.from_numpy(inp["w"].view(np.int16)).view(torch.bfloat16).to(dev)
+    q, sc = torch.from_numpy(inp["w_fp8"]).to(dev), torch.from_numpy(inp["w_scale"]).to(dev)
+    w16 = [w] + [w.clone() for _ in range(max(1, -(-(512 << 20) // (w.numel() * 2)) - 1))]
+    w8 = [(q, sc)] + [(q.clone(), sc.clone()) for _ in range(max(1, -(-(512 << 20) // q.numel()) - 1))]
+    out = []
+    for B in (32, 64):
+        x = torch.from_numpy(synth.bf16_normal((B, w.shape[1]), 1.0, 5, 77).view(np.int16)).view(torch.bfloat16).to(dev)
+        ws = tt.lm_head_workspace(B, c["vocab"], c["tp"], c["rank"], dev)
+        for shape in shapes:
+            for fp8 in (False, True):
+                print(f"lm-shapes: B {B} shape {shape} {'fp8' if fp8 else 'bf16'}", file=sys.stderr, flush=True)
+
+                def call(i):
+                    if fp8:
+                        qq, ss = w8[i % len(w8)]
+                        tt.lm_head_shard_argmax(x, c["vocab"], c["tp"], c["rank"], c["chunk"], qq,
+                                                tt.TP_DTYPE_FP8_E4M3, ss, workspace=ws)
+                    else:
+                        tt.lm_head_shard_argmax(x, c["vocab"], c["tp"], c["rank"], c["chunk"], w16[i % len(w16)],
+                                                workspace=ws)
+                with tt.tuning(lm_shape=shape):
+                    for i in range(5):
+                        call(i)
+                    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(20)]
+                    torch.cuda.synchronize()
+                    for i, (a, b) in enumerate(ev):
+                        a.record()
+                        call(i)
+                        b.record()
+                    torch.cuda.synchronize()
+                t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+                out.append({"batch_rows": B, "shape": shape, "weights": "fp8" if fp8 else "bf16",
+                            "call_median_us": round(t[10], 2)})
+    print(json.dumps({"lm_shapes": out}), flush=True)
+
+
+def stream_probe(n: int) -> None:
+    """The tuning library's fetch-shape probe over a bf16 LM-head weight shard (16032 rows x
+    8192 bytes) rotating over five copies: n launches per shape, HIP events per launch."""
+    import torch
+
+    import tensor_transformer_linear_amd as tt
+
+    rows, rowb = 16032, 8192
+    copies = [torch.full((rows * rowb,), 17, dtype=torch.uint8, device="cuda") for _ in range(5)]
+    out = torch.zeros(rows // 64 + 1, dtype=torch.int32, device="cuda")
+    T = tt.tuning_lib()
+    stream = torch.cuda.current_stream()
+    names = ["16 rows x 64 B", "8 rows x 128 B", "4 rows x 256 B", "1 row x 1 KB, rows interleaved",
+             "1 row x 1 KB, each wave's rows in order", "each 64-row block in order"]
+    res = []
+    for shape, nt in [(s, 1) for s in range(6)] + [(0, 0), (5, 0)]:
+        print(f"stream-probe: shape {shape} nontemporal {nt}", file=sys.stderr, flush=True)
+        t = []
+        for i in range(n + 3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = T.tpt_stream_probe(shape, nt, copies[i % 5].data_ptr(), rows, out.data_ptr(),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            b.record(stream)
+            if st != 0:
+                raise RuntimeError(f"tpt_stream_probe returned {st}")
+            b.synchronize()
+            if i >= 3:
+                t.append(a.elapsed_time(b) * 1e3)
+        t.sort()
+        med = t[len(t) // 2]
+        res.append({"shape": shape, "fetch": names[shape], "nontemporal": nt, "median_us": round(med, 2),
+                    "min_us": round(t[0], 2), "gbs": round(rows * rowb / med / 1e3, 1)})
+    print(json.dumps({"stream_probe": res, "bytes": rows * rowb, "launches": n}), flush=True)
+
+
 def copy_probe(mb: int):
     """Plain device-to-device copies of a known size: the reference for HBM byte counters."""
     import torch
@@ -640,7 +733,7 @@ def copy_probe(mb: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build emulates tensor-parallel ranks shard by shard on a "
+        print(f"bench.py runs on one GPU: the library computes tensor-parallel ranks shard by shard on a "
               f"single device and has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -654,6 +747,12 @@ def main():
         return
     if args.gemm_launches > 0:
         gemm_launches(args.gemm_launches)
+        return
+    if args.lm_shapes:
+        lm_shapes([int(v) for v in args.lm_shapes.split(",") if v])
+        return
+    if args.stream_probe > 0:
+        stream_probe(args.stream_probe)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

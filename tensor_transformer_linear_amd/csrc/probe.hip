@@ -7,6 +7,11 @@
 //  * v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, unit scales): A [32][64] E4M3, lane l holds row
 //    l % 32, K 32 (l / 32) .. +32.
 // The accumulator layout: lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4.
+//
+// A second probe streams a weight shard of 8192-byte rows once, as the LM head reads it
+// (workgroups of 8 waves owning 64-row blocks, two sets of 16 in-flight 16-byte loads per
+// lane, no arithmetic), in one of several fetch shapes: which rows and bytes one load
+// instruction covers. It measures what the access pattern alone costs.
 #include <string.h>
 
 #include "common.h"
@@ -45,7 +50,89 @@ __global__ __launch_bounds__(64) void mfma_row_sums_kernel(const unsigned char* 
   }
 }
 
+constexpr int SP_ROWB = 8192, SP_ROWS = 64;
+
+// Byte offset, in the workgroup's 64-row block, of the 16 bytes lane `lane` of wave `w` loads at
+// instruction i (0..63); every shape covers the block's 512 KB exactly once.
+template <int SHAPE>
+__device__ __forceinline__ int sp_off(int w, int lane, int i) {
+  if constexpr (SHAPE == 0) {  // 16 rows x 64 B: lane l on row l % 16 (the 16x16 MFMA operand layout)
+    const int row = (w & 3) * 16 + (lane & 15);
+    return row * SP_ROWB + (w >> 2) * 4096 + i * 64 + 16 * (lane >> 4);
+  } else if constexpr (SHAPE == 1) {  // 8 rows x 128 B
+    return (8 * w + (lane >> 3)) * SP_ROWB + i * 128 + 16 * (lane & 7);
+  } else if constexpr (SHAPE == 2) {  // 4 rows x 256 B (the row-quad LM-head kernel)
+    const int row = (w & 3) * 16 + (i / 16) * 4 + (lane >> 4);
+    return row * SP_ROWB + (w >> 2) * 4096 + (i % 16) * 256 + 16 * (lane & 15);
+  } else if constexpr (SHAPE == 3) {  // 1 row x 1 KB, the wave's 8 rows interleaved
+    return (8 * w + i % 8) * SP_ROWB + (i / 8) * 1024 + 16 * lane;
+  } else if constexpr (SHAPE == 4) {  // 1 row x 1 KB, each wave its 64 KB in order
+    return (8 * w + i / 8) * SP_ROWB + (i % 8) * 1024 + 16 * lane;
+  } else {  // 5: the workgroup's 512 KB in order, waves interleaved by 1 KB
+    return (i * 8 + w) * 1024 + 16 * lane;
+  }
+}
+
+template <int SHAPE, bool NT>
+__global__ __launch_bounds__(512) void stream_probe_kernel(const unsigned char* w, int rows, unsigned* out) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the last block is clamped to the shard's last 64 rows (reads stay in bounds)
+  const int r0 = min((int)blockIdx.x * SP_ROWS, rows - SP_ROWS);
+  const unsigned char* base = w + (int64_t)r0 * SP_ROWB;
+  unsigned acc = 0;
+  u32x4_t a[16], b[16];
+  auto ld = [&](u32x4_t* d, int set) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + sp_off<SHAPE>(wv, lane, set * 16 + j));
+      d[j] = NT ? __builtin_nontemporal_load(p) : *p;
+    }
+  };
+  auto use = [&](const u32x4_t* d) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += d[j][0] ^ d[j][1] ^ d[j][2] ^ d[j][3];
+  };
+  ld(a, 0);
+  ld(b, 1);
+  use(a);
+  ld(a, 2);
+  use(b);
+  ld(b, 3);
+  use(a);
+  use(b);
+  if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;  // keeps the loads; practically never stores
+}
+
+template <int SHAPE>
+void launch_stream_probe(bool nt, const unsigned char* w, int rows, unsigned* out, hipStream_t s) {
+  const int grid = (rows + SP_ROWS - 1) / SP_ROWS;
+  if (nt)
+    hipLaunchKernelGGL((stream_probe_kernel<SHAPE, true>), dim3(grid), dim3(512), 0, s, w, rows, out);
+  else
+    hipLaunchKernelGGL((stream_probe_kernel<SHAPE, false>), dim3(grid), dim3(512), 0, s, w, rows, out);
+}
+
 }  // namespace
+
+extern "C" TP_API int tpt_stream_probe(int shape, int nontemporal, const void* w, int64_t rows, void* out,
+                                       void* stream) {
+  if (w == nullptr || out == nullptr) return TP_ERR_INVALID_ARG;
+  if (shape < 0 || shape > 5 || rows < SP_ROWS || rows > (int64_t)1 << 20) return TP_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(out) & 3)) return TP_ERR_UNSUPPORTED;
+  const unsigned char* wp = static_cast<const unsigned char*>(w);
+  unsigned* op = static_cast<unsigned*>(out);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool nt = nontemporal != 0;
+  switch (shape) {
+    case 0: launch_stream_probe<0>(nt, wp, (int)rows, op, s); break;
+    case 1: launch_stream_probe<1>(nt, wp, (int)rows, op, s); break;
+    case 2: launch_stream_probe<2>(nt, wp, (int)rows, op, s); break;
+    case 3: launch_stream_probe<3>(nt, wp, (int)rows, op, s); break;
+    case 4: launch_stream_probe<4>(nt, wp, (int)rows, op, s); break;
+    default: launch_stream_probe<5>(nt, wp, (int)rows, op, s); break;
+  }
+  return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_HIP;
+}
 
 extern "C" TP_API int tpt_mfma_row_sums(int fp8, const void* a, const float* c, float* out, void* stream) {
   if (a == nullptr || c == nullptr || out == nullptr) return TP_ERR_INVALID_ARG;

@@ -217,6 +217,16 @@ def test_tuning_choices_checked_before_anything_else():
     assert tt.gemm_pick_tile(32768, 3072, 8192) in tt.GEMM_TILES
 
 
+def test_stream_probe_host_checks():
+    # refused on the host before any launch (no GPU needed)
+    T = tt.tuning_lib()
+    assert T.tpt_stream_probe(6, 1, A, 64, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_stream_probe(-1, 1, A, 64, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_stream_probe(2, 1, A, 63, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_stream_probe(2, 1, None, 64, A2, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_stream_probe(2, 1, ctypes.c_void_p(0x40008), 64, A2, None) == tt.TP_ERR_UNSUPPORTED
+
+
 def test_tuning_routing_restores_the_product_library():
     assert getattr(tt._tls, "choices", None) is None
     with tt.tuning(tile=3):
