@@ -60,6 +60,11 @@ def parse():
                     help="only run the decode LM head (workload 5 with 32 and 64 batch rows, bf16 and E4M3 "
                          "weights) under each listed launch shape (keys of LM_HEAD_SHAPES, through the tuning "
                          "library), 25 calls each, and exit; a kernel trace of this run gives the kernel times")
+    ap.add_argument("--mfma-rate", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the tuning library's matrix-rate probe (independent bf16 MFMAs, no memory "
+                         "traffic) back to back for about SECONDS and report its TFLOP/s cold and sustained")
+    ap.add_argument("--mfma-rate-workgroups", type=int, default=1024, metavar="W",
+                    help="workgroups of 4 waves per --mfma-rate launch (1024: four waves per SIMD; 256: one)")
     ap.add_argument("--stream-probe", type=int, default=0, metavar="N",
                     help="only stream a bf16 LM-head weight shard (16032 rows x 8192 bytes, rotated copies) N "
                          "times in each fetch shape of the tuning library's probe and exit")
@@ -717,6 +722,47 @@ def stream_probe(n: int) -> None:
     print(json.dumps({"stream_probe": res, "bytes": rows * rowb, "launches": n}), flush=True)
 
 
+def mfma_rate(seconds: float, wgs: int) -> None:
+    """The matrix rate the chip sustains: the tuning library's probe (``wgs`` workgroups of 4
+    waves, each wave 4 independent v_mfma_f32_32x32x16_bf16 chains on pseudo-random operands,
+    4000 rounds: 2.15 TFLOP per launch at 1024 workgroups) back to back for about ``seconds``,
+    HIP events per launch."""
+    import torch
+
+    import tensor_transformer_linear_amd as tt
+
+    iters = 4000
+    flops = wgs * 4 * iters * 4 * 32 * 32 * 16 * 2
+    out = torch.zeros(wgs, dtype=torch.float32, device="cuda")
+    T = tt.tuning_lib()
+    stream = torch.cuda.current_stream()
+    h = ctypes.c_void_p(stream.cuda_stream)
+    t_ms = []
+    t0 = time.perf_counter()
+    last = t0
+    while time.perf_counter() - t0 < seconds:
+        batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for a, b in batch:
+            a.record(stream)
+            if T.tpt_mfma_rate(wgs, iters, out.data_ptr(), h) != 0:
+                raise RuntimeError("tpt_mfma_rate failed")
+            b.record(stream)
+        torch.cuda.synchronize()
+        t_ms += [a.elapsed_time(b) for a, b in batch]
+        if time.perf_counter() - last > 1.0:
+            last = time.perf_counter()
+            print(f"mfma-rate: {len(t_ms)} launches, last {flops / t_ms[-1] / 1e9:.0f} TFLOP/s", file=sys.stderr,
+                  flush=True)
+    tf = [flops / t / 1e9 for t in t_ms]
+    tail = sorted(tf[len(tf) * 4 // 5:])
+    print(json.dumps({"mfma_rate": {"workgroups": wgs, "waves_per_simd": wgs * 4 // 1024, "flops_per_launch": flops,
+                                    "launches": len(tf), "seconds": round(sum(t_ms) / 1e3, 2),
+                                    "first_5_median_tflops": round(float(np.median(tf[:5])), 1),
+                                    "last_fifth_median_tflops": round(tail[len(tail) // 2], 1),
+                                    "max_tflops": round(max(tf), 1), "peak_bf16_tflops": PEAK_BF16_TFLOPS}}),
+          flush=True)
+
+
 def copy_probe(mb: int):
     """Plain device-to-device copies of a known size: the reference for HBM byte counters."""
     import torch
@@ -753,6 +799,9 @@ def main():
         return
     if args.stream_probe > 0:
         stream_probe(args.stream_probe)
+        return
+    if args.mfma_rate > 0:
+        mfma_rate(args.mfma_rate, args.mfma_rate_workgroups)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
