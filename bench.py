@@ -707,9 +707,11 @@ def stream_probe(n: int) -> None:
     T = tt.tuning_lib()
     stream = torch.cuda.current_stream()
     names = ["16 rows x 64 B", "8 rows x 128 B", "4 rows x 256 B", "1 row x 1 KB, rows interleaved",
-             "1 row x 1 KB, each wave's rows in order", "each 64-row block in order"]
+             "1 row x 1 KB, each wave's rows in order", "each 64-row block in order",
+             "4 rows x 256 B in the row-quad kernel's window order",
+             "4 rows x 256 B in the row-quad kernel's window order, staggered slices"]
     res = []
-    for shape, nt in [(s, 1) for s in range(6)] + [(0, 0), (5, 0)]:
+    for shape, nt in [(s, 1) for s in range(8)] + [(0, 0), (5, 0)]:
         print(f"stream-probe: shape {shape} nontemporal {nt}", file=sys.stderr, flush=True)
         t = []
         for i in range(n + 3):

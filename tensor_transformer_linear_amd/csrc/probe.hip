@@ -59,7 +59,7 @@ constexpr int SP_ROWB = 8192, SP_ROWS = 64;
 // Byte offset, in the workgroup's 64-row block, of the 16 bytes lane `lane` of wave `w` loads at
 // instruction i (0..63); every shape covers the block's 512 KB exactly once.
 template <int SHAPE>
-__device__ __forceinline__ int sp_off(int w, int lane, int i) {
+__device__ __forceinline__ int sp_off(int w, int lane, int i, int blk) {
   if constexpr (SHAPE == 0) {  // 16 rows x 64 B: lane l on row l % 16 (the 16x16 MFMA operand layout)
     const int row = (w & 3) * 16 + (lane & 15);
     return row * SP_ROWB + (w >> 2) * 4096 + i * 64 + 16 * (lane >> 4);
@@ -72,8 +72,13 @@ __device__ __forceinline__ int sp_off(int w, int lane, int i) {
     return (8 * w + i % 8) * SP_ROWB + (i / 8) * 1024 + 16 * lane;
   } else if constexpr (SHAPE == 4) {  // 1 row x 1 KB, each wave its 64 KB in order
     return (8 * w + i / 8) * SP_ROWB + (i % 8) * 1024 + 16 * lane;
-  } else {  // 5: the workgroup's 512 KB in order, waves interleaved by 1 KB
+  } else if constexpr (SHAPE == 5) {  // the workgroup's 512 KB in order, waves interleaved by 1 KB
     return (i * 8 + w) * 1024 + 16 * lane;
+  } else {  // 6, 7: the row-quad kernel's order: window i / 4 of the wave's K half of each 512-byte
+            // slice; 7 visits the slices from slice (block mod 16) on, wrapping, as that kernel does
+    const int row = (w & 3) * 16 + 4 * (i % 4) + (lane >> 4);
+    const int slice = SHAPE == 7 ? (i / 4 + blk) % 16 : i / 4;
+    return row * SP_ROWB + slice * 512 + (w >> 2) * 256 + 16 * (lane & 15);
   }
 }
 
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(512) void stream_probe_kernel(const unsigned char* 
   auto ld = [&](u32x4_t* d, int set) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + sp_off<SHAPE>(wv, lane, set * 16 + j));
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + sp_off<SHAPE>(wv, lane, set * 16 + j, blockIdx.x));
       d[j] = NT ? __builtin_nontemporal_load(p) : *p;
     }
   };
@@ -166,7 +171,7 @@ extern "C" TP_API int tpt_mfma_rate(int workgroups, int iters, void* out, void* 
 extern "C" TP_API int tpt_stream_probe(int shape, int nontemporal, const void* w, int64_t rows, void* out,
                                        void* stream) {
   if (w == nullptr || out == nullptr) return TP_ERR_INVALID_ARG;
-  if (shape < 0 || shape > 5 || rows < SP_ROWS || rows > (int64_t)1 << 20) return TP_ERR_SHAPE;
+  if (shape < 0 || shape > 7 || rows < SP_ROWS || rows > (int64_t)1 << 20) return TP_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(out) & 3)) return TP_ERR_UNSUPPORTED;
   const unsigned char* wp = static_cast<const unsigned char*>(w);
   unsigned* op = static_cast<unsigned*>(out);
@@ -178,7 +183,9 @@ extern "C" TP_API int tpt_stream_probe(int shape, int nontemporal, const void* w
     case 2: launch_stream_probe<2>(nt, wp, (int)rows, op, s); break;
     case 3: launch_stream_probe<3>(nt, wp, (int)rows, op, s); break;
     case 4: launch_stream_probe<4>(nt, wp, (int)rows, op, s); break;
-    default: launch_stream_probe<5>(nt, wp, (int)rows, op, s); break;
+    case 5: launch_stream_probe<5>(nt, wp, (int)rows, op, s); break;
+    case 6: launch_stream_probe<6>(nt, wp, (int)rows, op, s); break;
+    default: launch_stream_probe<7>(nt, wp, (int)rows, op, s); break;
   }
   return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_HIP;
 }

@@ -65,10 +65,12 @@ TP_API int tpt_mfma_row_sums(int fp8, const void* a, const float* c, float* out,
 /* Streams `rows` rows of 8192 bytes (w: device, 16-byte aligned, rows >= 64) once with 16-byte
  * loads in fetch shape `shape` (what one load instruction covers: 0 = 16 rows x 64 B, 1 = 8 rows
  * x 128 B, 2 = 4 rows x 256 B, 3 = 1 row x 1 KB with the wave's rows interleaved, 4 = 1 row x 1 KB
- * with each wave's 64 KB in order, 5 = each 64-row block in order), non-temporal if
+ * with each wave's 64 KB in order, 5 = each 64-row block in order, 6 = the row-quad LM-head
+ * kernel's order: 4 rows x 256 B, window by window over the wave's half of each 512-byte slice;
+ * 7 = 6 with the slices visited from slice (block mod 16) on), non-temporal if
  * `nontemporal`; one workgroup of 8 waves per 64-row block (the last block clamped to the last
  * 64 rows). out: device, 4 bytes per block, written only in the practically impossible case
- * that the loaded words reduce to a fixed value. TP_ERR_SHAPE for a shape outside 0..5 or rows
+ * that the loaded words reduce to a fixed value. TP_ERR_SHAPE for a shape outside 0..7 or rows
  * outside [64, 2^20]. */
 TP_API int tpt_stream_probe(int shape, int nontemporal, const void* w, int64_t rows, void* out, void* stream);
 

@@ -220,7 +220,7 @@ def test_tuning_choices_checked_before_anything_else():
 def test_stream_probe_host_checks():
     # refused on the host before any launch (no GPU needed)
     T = tt.tuning_lib()
-    assert T.tpt_stream_probe(6, 1, A, 64, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_stream_probe(8, 1, A, 64, A2, None) == tt.TP_ERR_SHAPE
     assert T.tpt_stream_probe(-1, 1, A, 64, A2, None) == tt.TP_ERR_SHAPE
     assert T.tpt_stream_probe(2, 1, A, 63, A2, None) == tt.TP_ERR_SHAPE
     assert T.tpt_stream_probe(2, 1, None, 64, A2, None) == tt.TP_ERR_INVALID_ARG
