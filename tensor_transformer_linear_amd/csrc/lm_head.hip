@@ -793,9 +793,9 @@ __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem
 // g = w % 4 (16 rows) over K half h = w / 4 of every x slice, x sits in LDS one slice of XS_K
 // columns at a time (double-buffered), and the weight goes to registers with non-temporal
 // 16-byte loads. What differs is the fetch shape. The operand layout wants 16 rows x 64
-// bytes per load instruction, and that shape streamed about 25% slower on this GPU than
-// 4 rows x 256 contiguous bytes, the fastest of the shapes measured (the same as a linear
-// sweep of the workgroup's rows). So here lane l of a load reads row l / 16 at bytes
+// bytes per load instruction, and that shape streamed about 30% slower on this GPU than
+// 4 rows x 256 contiguous bytes, the fastest of the shapes measured (as fast as a linear
+// sweep of the workgroup's rows; tpt_stream_probe). So here lane l of a load reads row l / 16 at bytes
 // 16 (l % 16) of a 256-byte run, and a "window" is four such loads: 16 rows x 256 bytes
 // (128 bf16 or 256 E4M3 K values). The wave writes its window to its own 4 KB of LDS and
 // reads it back in the operand layout (lane l: row l % 16, 16 bytes at chunk 4 t + l / 16 for
@@ -805,9 +805,9 @@ __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem
 // D windows of weight loads are in flight. A slice's x loads are issued just before the
 // weight loads of the slice's first window, so that waiting for them (before they are
 // written to LDS at the end of the previous slice) never waits for a weight load that is
-// not needed yet; two register sets hold them, which bounds D by twice the windows per
-// slice. Slices are visited from slice (tile mod slice count) on, wrapping, so that the
-// tiles in flight read different offsets of their rows (as in the LDS-ring kernel).
+// not needed yet; NXS register sets hold them, which bounds D by NXS times the windows per
+// slice. With ROT, slices are visited from slice (tile mod slice count) on, wrapping, so that
+// the tiles in flight read different offsets of their rows (as in the LDS-ring kernel).
 //
 // Operand layout for v_mfma_f32_16x16x32_bf16 is the x-resident kernel's: x the row operand,
 // the weight the column operand; bf16 step t of a window takes K values 32 t + 8 q .. +8
