@@ -65,6 +65,8 @@ def parse():
                          "traffic) back to back for about SECONDS and report its TFLOP/s cold and sustained")
     ap.add_argument("--mfma-rate-workgroups", type=int, default=1024, metavar="W",
                     help="workgroups of 4 waves per --mfma-rate launch (1024: four waves per SIMD; 256: one)")
+    ap.add_argument("--mfma-rate-fp8", type=int, default=0, metavar="0|1",
+                    help="1: --mfma-rate runs the E4M3 instruction (v_mfma_scale_f32_32x32x64_f8f6f4)")
     ap.add_argument("--stream-probe", type=int, default=0, metavar="N",
                     help="only stream a bf16 LM-head weight shard (16032 rows x 8192 bytes, rotated copies) N "
                          "times in each fetch shape of the tuning library's probe and exit")
@@ -732,17 +734,18 @@ def stream_probe(n: int) -> None:
     print(json.dumps({"stream_probe": res, "bytes": rows * rowb, "launches": n}), flush=True)
 
 
-def mfma_rate(seconds: float, wgs: int) -> None:
+def mfma_rate(seconds: float, wgs: int, fp8: int) -> None:
     """The matrix rate the chip sustains: the tuning library's probe (``wgs`` workgroups of 4
-    waves, each wave 4 independent v_mfma_f32_32x32x16_bf16 chains on pseudo-random operands,
-    4000 rounds: 2.15 TFLOP per launch at 1024 workgroups) back to back for about ``seconds``,
+    waves, each wave 4 independent v_mfma_f32_32x32x16_bf16 chains, or with ``fp8``
+    v_mfma_scale_f32_32x32x64_f8f6f4 chains, on pseudo-random operands; 4000 rounds, 2000 for
+    E4M3: 2.15 or 4.29 TFLOP per launch at 1024 workgroups) back to back for about ``seconds``,
     HIP events per launch."""
     import torch
 
     import tensor_transformer_linear_amd as tt
 
-    iters = 4000
-    flops = wgs * 4 * iters * 4 * 32 * 32 * 16 * 2
+    iters = 2000 if fp8 else 4000
+    flops = wgs * 4 * iters * 4 * 32 * 32 * (64 if fp8 else 16) * 2
     out = torch.zeros(wgs, dtype=torch.float32, device="cuda")
     T = tt.tuning_lib()
     stream = torch.cuda.current_stream()
@@ -754,7 +757,7 @@ def mfma_rate(seconds: float, wgs: int) -> None:
         batch = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
         for a, b in batch:
             a.record(stream)
-            if T.tpt_mfma_rate(wgs, iters, out.data_ptr(), h) != 0:
+            if T.tpt_mfma_rate(fp8, wgs, iters, out.data_ptr(), h) != 0:
                 raise RuntimeError("tpt_mfma_rate failed")
             b.record(stream)
         torch.cuda.synchronize()
@@ -765,11 +768,13 @@ def mfma_rate(seconds: float, wgs: int) -> None:
                   flush=True)
     tf = [flops / t / 1e9 for t in t_ms]
     tail = sorted(tf[len(tf) * 4 // 5:])
-    print(json.dumps({"mfma_rate": {"workgroups": wgs, "waves_per_simd": wgs * 4 // 1024, "flops_per_launch": flops,
+    print(json.dumps({"mfma_rate": {"instruction": "v_mfma_scale_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_f32_32x32x16_bf16",
+                                    "workgroups": wgs, "waves_per_simd": wgs * 4 // 1024, "flops_per_launch": flops,
                                     "launches": len(tf), "seconds": round(sum(t_ms) / 1e3, 2),
                                     "first_5_median_tflops": round(float(np.median(tf[:5])), 1),
                                     "last_fifth_median_tflops": round(tail[len(tail) // 2], 1),
-                                    "max_tflops": round(max(tf), 1), "peak_bf16_tflops": PEAK_BF16_TFLOPS}}),
+                                    "max_tflops": round(max(tf), 1),
+                                    "peak_tflops": PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS}}),
           flush=True)
 
 
@@ -811,7 +816,7 @@ def main():
         stream_probe(args.stream_probe)
         return
     if args.mfma_rate > 0:
-        mfma_rate(args.mfma_rate, args.mfma_rate_workgroups)
+        mfma_rate(args.mfma_rate, args.mfma_rate_workgroups, args.mfma_rate_fp8)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -85,7 +85,7 @@ TUNING_SIGNATURES = {
     "tpt_lm_head_shape_count": (_int, []),
     "tpt_mfma_row_sums": (_int, [_int, _vp, _vp, _vp, _vp]),
     "tpt_stream_probe": (_int, [_int, _int, _vp, _i64, _vp, _vp]),
-    "tpt_mfma_rate": (_int, [_int, _int, _vp, _vp]),
+    "tpt_mfma_rate": (_int, [_int, _int, _int, _vp, _vp]),
     "tp_last_error": (ctypes.c_char_p, []),
 }
 

@@ -13,9 +13,10 @@
 // lane, no arithmetic), in one of several fetch shapes: which rows and bytes one load
 // instruction covers. It measures what the access pattern alone costs.
 //
-// A third runs nothing but independent v_mfma_f32_32x32x16_bf16 instructions (four accumulator
-// chains per wave on four pseudo-random operand pairs in registers, no memory traffic in the
-// loop): the matrix rate the chip sustains, cold and at its power cap.
+// A third runs nothing but independent v_mfma_f32_32x32x16_bf16 (or, for E4M3,
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales) instructions: four accumulator chains per
+// wave on four pseudo-random operand pairs in registers, no memory traffic in the loop. It
+// measures the matrix rate the chip sustains, cold and under sustained load.
 #include <string.h>
 
 #include "common.h"
@@ -121,50 +122,73 @@ void launch_stream_probe(bool nt, const unsigned char* w, int rows, unsigned* ou
     hipLaunchKernelGGL((stream_probe_kernel<SHAPE, false>), dim3(grid), dim3(512), 0, s, w, rows, out);
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void mfma_rate_kernel(int iters, float* out) {
   const uint32_t lane = threadIdx.x & 63;
-  // Four operand pairs of pseudo-random bf16 values in [1, 2) x random signs (an integer hash of
-  // lane and index): consecutive instructions take different pairs, so the multipliers switch
-  // as they do on real data. The values themselves do not matter.
-  bf16x8_t a[4], b[4];
+  // Four operand pairs of pseudo-random values (an integer hash of lane and index): bf16 in
+  // [1, 2) with random signs, or E4M3 codes with random signs, mantissas and exponents 6..9.
+  // Consecutive instructions take different pairs, so the multipliers switch as they do on
+  // real data. The values themselves do not matter.
+  constexpr int NW = FP8 ? 8 : 4;  // 32-bit words per operand: 32 E4M3 or 8 bf16 values
+  uint32_t av[4][NW], bv[4][NW];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    u32x4_t av, bv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t h = (lane * 4u + (uint32_t)i) * 0x9E3779B1u + (uint32_t)j * 0x85EBCA77u;
+    for (int i = 0; i < NW; ++i) {
+      uint32_t h = (lane * 8u + (uint32_t)i) * 0x9E3779B1u + (uint32_t)j * 0x85EBCA77u;
       h ^= h >> 15;
       h *= 0x2C1B3C6Du;
       h ^= h >> 13;
-      av[i] = (h & 0x807F807Fu) | 0x3F803F80u;
-      bv[i] = ((h >> 7) & 0x807F807Fu) | 0x3F803F80u;
+      if constexpr (FP8) {
+        av[j][i] = (h & 0x87878787u) | 0x30303030u;
+        bv[j][i] = ((h >> 3) & 0x87878787u) | 0x30303030u;
+      } else {
+        av[j][i] = (h & 0x807F807Fu) | 0x3F803F80u;
+        bv[j][i] = ((h >> 7) & 0x807F807Fu) | 0x3F803F80u;
+      }
     }
-    a[j] = __builtin_bit_cast(bf16x8_t, av);
-    b[j] = __builtin_bit_cast(bf16x8_t, bv);
   }
-  f32x16_t c0, c1, c2, c3;
+  f32x16_t c[4];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) c0[v] = c1[v] = c2[v] = c3[v] = 0.0f;
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c[j][v] = 0.0f;
   for (int it = 0; it < iters; ++it) {
-    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c1, 0, 0, 0);
-    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[2], c2, 0, 0, 0);
-    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[3], c3, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FP8) {
+        i32x8_t A, B;
+        memcpy(&A, av[j], 32);
+        memcpy(&B, bv[j], 32);
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c[j], 0, 0, 0, 0, 0, 0);
+      } else {
+        u32x4_t a4, b4;
+        memcpy(&a4, av[j], 16);
+        memcpy(&b4, bv[j], 16);
+        c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a4), __builtin_bit_cast(bf16x8_t, b4),
+                                                       c[j], 0, 0, 0);
+      }
+    }
   }
   float t = 0.0f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) t += c0[v] + c1[v] + c2[v] + c3[v];
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t += c[j][v];
   if (t == 1234.5f) out[blockIdx.x] = t;  // keeps the chains; practically never stores
 }
 
 }  // namespace
 
-extern "C" TP_API int tpt_mfma_rate(int workgroups, int iters, void* out, void* stream) {
+extern "C" TP_API int tpt_mfma_rate(int fp8, int workgroups, int iters, void* out, void* stream) {
   if (out == nullptr) return TP_ERR_INVALID_ARG;
   if (workgroups < 1 || workgroups > (1 << 20) || iters < 1) return TP_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(out) & 3) return TP_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mfma_rate_kernel, dim3(workgroups), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), iters,
-                     static_cast<float*>(out));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (fp8)
+    hipLaunchKernelGGL(mfma_rate_kernel<true>, dim3(workgroups), dim3(256), 0, s, iters, static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel<false>, dim3(workgroups), dim3(256), 0, s, iters, static_cast<float*>(out));
   return hipGetLastError() == hipSuccess ? TP_OK : TP_ERR_HIP;
 }
 

@@ -75,10 +75,11 @@ TP_API int tpt_mfma_row_sums(int fp8, const void* a, const float* c, float* out,
 TP_API int tpt_stream_probe(int shape, int nontemporal, const void* w, int64_t rows, void* out, void* stream);
 
 /* `workgroups` workgroups of 4 waves, each wave running `iters` rounds of four independent
- * v_mfma_f32_32x32x16_bf16 (32768 flops each) on register operands: 4 * 4 * 32768 * iters flops per
- * workgroup, no memory traffic. out: device, 4 bytes per workgroup, practically never written.
- * TP_ERR_SHAPE for workgroups outside [1, 2^20] or iters < 1. */
-TP_API int tpt_mfma_rate(int workgroups, int iters, void* out, void* stream);
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each; fp8 = 1: v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3,
+ * 131072 flops each) on pseudo-random register operands, no memory traffic. out: device, 4 bytes
+ * per workgroup, practically never written. TP_ERR_SHAPE for workgroups outside [1, 2^20] or
+ * iters < 1. */
+TP_API int tpt_mfma_rate(int fp8, int workgroups, int iters, void* out, void* stream);
 
 #ifdef __cplusplus
 }

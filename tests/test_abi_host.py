@@ -225,9 +225,9 @@ def test_stream_probe_host_checks():
     assert T.tpt_stream_probe(2, 1, A, 63, A2, None) == tt.TP_ERR_SHAPE
     assert T.tpt_stream_probe(2, 1, None, 64, A2, None) == tt.TP_ERR_INVALID_ARG
     assert T.tpt_stream_probe(2, 1, ctypes.c_void_p(0x40008), 64, A2, None) == tt.TP_ERR_UNSUPPORTED
-    assert T.tpt_mfma_rate(0, 10, A2, None) == tt.TP_ERR_SHAPE
-    assert T.tpt_mfma_rate(8, 0, A2, None) == tt.TP_ERR_SHAPE
-    assert T.tpt_mfma_rate(8, 10, None, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_mfma_rate(0, 0, 10, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_mfma_rate(1, 8, 0, A2, None) == tt.TP_ERR_SHAPE
+    assert T.tpt_mfma_rate(0, 8, 10, None, None) == tt.TP_ERR_INVALID_ARG
 
 
 def test_tuning_routing_restores_the_product_library():
