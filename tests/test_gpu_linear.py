@@ -232,7 +232,8 @@ def test_paired_k_rows_tile_integer_exact(tile, K):
     last pair), a few pairs (every issue past the end reloads it), and 21 pairs (the ring of 5
     or 10 halves wraps several times; unequal A and B halves for the non-square tiles). Ragged
     M and N, a sub-parameter boundary inside the tile, bias, GELU; bit-exact on integer
-    inputs."""
+    inputs, for every output mode (bf16, bf16 + GELU, float32, float32 + GELU, float32
+    accumulate)."""
     tt.set_gemm_tile(tile)
     tt.set_gemm_path(tt.GEMM_PATH_DMA)
     M, sizes, tp, rank = 301, [300, 76, 76], 2, 1
@@ -243,6 +244,12 @@ def test_paired_k_rows_tile_integer_exact(tile, K):
     yg = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, act=tt.TP_ACT_GELU_ERF)
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(yg), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=tt.TP_ACT_GELU_ERF))
+    # float32 output with GELU: the runtime-mode output stage
+    yfg = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, act=tt.TP_ACT_GELU_ERF,
+                              y_dtype=tt.TP_DTYPE_F32)
+    torch.cuda.synchronize()
+    ref = oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=tt.TP_ACT_GELU_ERF, out_dtype=oracle.OUT_F32)
+    assert assert_close(host_f32(yfg), ref, what="gelu f32") < 1e-4
     # bf16 output without activation, with and without bias (the kernels' bf16-only output stage)
     for bias_r in (b_r, None):
         yb = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), None if bias_r is None else dev_bf16(bias_r),
