@@ -155,6 +155,87 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
   return c;
 }
 
+// Output stage of the bf16-output modes without fp8 scales (EPI_BF16, EPI_BF16_GELU): bias and
+// GELU are applied in registers, each value is rounded once, and the band is parked in LDS as
+// bf16, half the bytes of the float32 stage below. Lanes 2c and 2c + 1 hold columns 2c and 2c + 1
+// of the same rows, and rows R(v) and R(v + 1) are adjacent for even v: the pair swaps one value
+// (a DPP move), then the even lane writes both columns of row R(v) and the odd lane both columns
+// of row R(v + 1), one 32-bit word each. The read-back takes eight columns (16 bytes) per thread.
+// The values and their rounding are those of the float32 stage, so the outputs are identical.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool GELU>
+__device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x16_t (&acc)[FM][FN],
+                                                     unsigned char* smem, int m0, int n0, int wm, int wn, int lane,
+                                                     int tid) {
+  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int SROW = BN + 8;        // staged row pitch in bf16 values (a 16-byte bank offset)
+  constexpr int SROWS = WAVES_M * 32;  // staged rows per band
+  constexpr int C8 = BN / 8;           // eight-column chunks per staged row
+  constexpr int Q = SROWS * C8 / NT;   // chunks per thread per band
+  static_assert(SROWS * C8 % NT == 0 && NT % C8 == 0, "band chunks must divide evenly, one column per thread");
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
+  const GemmEpilogue& ep = p.ep;
+  const int M = p.M, N = p.N;
+  float bias[FN];  // this lane's bias in each 32-column block
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    bias[j] = ep.bias != nullptr ? bf16_to_f32(ep.bias[min(n0 + wn * WN + j * 32 + (lane & 31), N - 1)]) : 0.0f;
+  // this thread's read-back columns (the same in every pass): their segment, and whether all
+  // eight share it and lie below N
+  const int c8 = tid % C8, col = n0 + c8 * 8;
+  const SegHit hit = seg_of(ep, col, {0, N});
+  const bool whole = col + 8 <= hit.end && col + 8 <= N;
+  const int odd = lane & 1;
+  const int wr_off = odd * (SROW - 1);  // odd lanes write the next row, one column to the left
+  static_for<FM>([&](auto i) {
+    static_for<FN>([&](auto j) {
+      static_for<8>([&](auto vp) {
+        constexpr int v = 2 * decltype(vp)::value;
+        float a = acc[i][j][v] + bias[j], b = acc[i][j][v + 1] + bias[j];
+        if constexpr (GELU) {
+          a = gelu_erf(a);
+          b = gelu_erf(b);
+        }
+        const uint32_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+        // quad_perm [1, 0, 3, 2]: each lane receives its pair partner's value
+        const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? ha : hb), 0xB1, 0xF, 0xF, false);
+        const uint32_t word = odd ? (recv | (hb << 16)) : (ha | (recv << 16));
+        const int r = wm * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        *reinterpret_cast<uint32_t*>(stage + r * SROW + wn * WN + j * 32 + (lane & 31) + wr_off) = word;
+      });
+    });
+    __syncthreads();
+    bool partial = false;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int sr = (tid + q * NT) / C8;
+      const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+      if (row < M && col < N) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc + col + hit.delta;
+        if (whole && (reinterpret_cast<uintptr_t>(out) & 15) == 0)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(stage + sr * SROW + c8 * 8),
+                                      reinterpret_cast<u32x4_t*>(out));
+        else
+          partial = true;
+      }
+    }
+    if (partial) {  // a chunk crossing a segment end or column N, or a misaligned output row
+#pragma unroll 1
+      for (int q = 0; q < Q; ++q) {
+        const int sr = (tid + q * NT) / C8;
+        const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+        if (row >= M || col >= N) continue;
+        uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc;
+        if (whole && (reinterpret_cast<uintptr_t>(out + col + hit.delta) & 15) == 0) continue;
+        const uint16_t* src = stage + sr * SROW + c8 * 8;
+#pragma unroll 1
+        for (int e = 0; e < 8 && col + e < N; ++e) out[col + e + seg_of(ep, col + e, {hit.delta, 0}).delta] = src[e];
+      }
+    }
+    __syncthreads();
+  });
+}
+
 // Output stage of a BM x BN tile, one 32-row band of every wave at a time. In a 32x32
 // accumulator block, lane l holds column l % 32 and rows 8 (v / 4) + 4 (l / 32) + v % 4 of
 // its sixteen values v. Each wave parks its band (32 rows x WN columns) in LDS; the
@@ -164,6 +245,11 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
 template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool MAPPED, int EPI = EPI_GENERIC>
 __device__ __forceinline__ void gemm_store_tile(const GemmProblem& p, f32x16_t (&acc)[FM][FN], unsigned char* smem,
                                                 int m0, int n0, int wm, int wn, int lane, int tid) {
+  if constexpr (!MAPPED && (EPI == EPI_BF16 || EPI == EPI_BF16_GELU)) {
+    gemm_store_tile_bf16<BM, BN, WAVES_M, WAVES_N, FM, FN, EPI == EPI_BF16_GELU>(p, acc, smem, m0, n0, wm, wn, lane,
+                                                                                 tid);
+    return;
+  }
   constexpr int NT = WAVES_M * WAVES_N * 64;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   const int M = p.M, N = p.N;
