@@ -162,6 +162,8 @@ __device__ __forceinline__ ChunkCols chunk_cols(const GemmEpilogue& ep, int col,
 // (a DPP move), then the even lane writes both columns of row R(v) and the odd lane both columns
 // of row R(v + 1), one 32-bit word each. The read-back takes eight columns (16 bytes) per thread.
 // The values and their rounding are those of the float32 stage, so the outputs are identical.
+// Only the paired-row kernels call it: `smem` is their free 160 KB ring, and the stage is the
+// kernel's last use of it.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int FM, int FN, bool GELU>
 __device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x16_t (&acc)[FM][FN],
                                                      unsigned char* smem, int m0, int n0, int wm, int wn, int lane,
@@ -187,7 +189,12 @@ __device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x1
   const bool whole = col + 8 <= hit.end && col + 8 <= N;
   const int odd = lane & 1;
   const int wr_off = odd * (SROW - 1);  // odd lanes write the next row, one column to the left
-  static_for<FM>([&](auto i) {
+  // Every band at once when they fit in the 160 KB the paired-row kernels' ring frees (one
+  // barrier per tile instead of two per band), else one band at a time.
+  constexpr int BAND = SROWS * SROW;
+  constexpr int PASS = FM * BAND * 2 <= 160 * 1024 ? FM : 1;  // bands per pass
+  auto park = [&](auto ic, int slot) {
+    constexpr int i = decltype(ic)::value;
     static_for<FN>([&](auto j) {
       static_for<8>([&](auto vp) {
         constexpr int v = 2 * decltype(vp)::value;
@@ -201,10 +208,12 @@ __device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x1
         const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? ha : hb), 0xB1, 0xF, 0xF, false);
         const uint32_t word = odd ? (recv | (hb << 16)) : (ha | (recv << 16));
         const int r = wm * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        *reinterpret_cast<uint32_t*>(stage + r * SROW + wn * WN + j * 32 + (lane & 31) + wr_off) = word;
+        *reinterpret_cast<uint32_t*>(stage + slot * BAND + r * SROW + wn * WN + j * 32 + (lane & 31) + wr_off) = word;
       });
     });
-    __syncthreads();
+  };
+  // stores band i from stage slot `slot`; returns whether a chunk was left to the element-wise pass
+  auto drain = [&](int i, int slot) {
     bool partial = false;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
@@ -213,27 +222,47 @@ __device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x1
       if (row < M && col < N) {
         uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc + col + hit.delta;
         if (whole && (reinterpret_cast<uintptr_t>(out) & 15) == 0)
-          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(stage + sr * SROW + c8 * 8),
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(stage + slot * BAND + sr * SROW + c8 * 8),
                                       reinterpret_cast<u32x4_t*>(out));
         else
           partial = true;
       }
     }
-    if (partial) {  // a chunk crossing a segment end or column N, or a misaligned output row
+    return partial;
+  };
+  // a chunk crossing a segment end or column N, or a misaligned output row
+  auto drain_partial = [&](int i, int slot) {
 #pragma unroll 1
-      for (int q = 0; q < Q; ++q) {
-        const int sr = (tid + q * NT) / C8;
-        const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
-        if (row >= M || col >= N) continue;
-        uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc;
-        if (whole && (reinterpret_cast<uintptr_t>(out + col + hit.delta) & 15) == 0) continue;
-        const uint16_t* src = stage + sr * SROW + c8 * 8;
+    for (int q = 0; q < Q; ++q) {
+      const int sr = (tid + q * NT) / C8;
+      const int row = m0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+      if (row >= M || col >= N) continue;
+      uint16_t* out = reinterpret_cast<uint16_t*>(ep.C) + (int64_t)row * ep.ldc;
+      if (whole && (reinterpret_cast<uintptr_t>(out + col + hit.delta) & 15) == 0) continue;
+      const uint16_t* src = stage + slot * BAND + sr * SROW + c8 * 8;
 #pragma unroll 1
-        for (int e = 0; e < 8 && col + e < N; ++e) out[col + e + seg_of(ep, col + e, {hit.delta, 0}).delta] = src[e];
-      }
+      for (int e = 0; e < 8 && col + e < N; ++e) out[col + e + seg_of(ep, col + e, {hit.delta, 0}).delta] = src[e];
     }
+  };
+  if constexpr (PASS == FM) {
+    static_for<FM>([&](auto i) { park(i, decltype(i)::value); });
     __syncthreads();
-  });
+    bool partial = false;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) partial |= drain(i, i);
+    if (partial) {
+#pragma unroll 1
+      for (int i = 0; i < FM; ++i) drain_partial(i, i);
+    }
+    // nothing reads or writes the stage after this: the kernel ends
+  } else {
+    static_for<FM>([&](auto i) {
+      park(i, 0);
+      __syncthreads();
+      if (drain(i, 0)) drain_partial(i, 0);
+      __syncthreads();
+    });
+  }
 }
 
 // Output stage of a BM x BN tile, one 32-row band of every wave at a time. In a 32x32
@@ -904,6 +933,8 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   static_assert((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && SLOTS >= 4 && VM_EVEN < 64, "pair ring shape");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SLOTS * HALF];
   static_assert(SLOTS * HALF >= WAVES_M * 32 * (BN + 4) * 4, "the output stage reuses the ring");
+  static_assert((EPI != EPI_BF16 && EPI != EPI_BF16_GELU) || SLOTS * HALF >= 160 * 1024,
+                "the bf16 output stage may park every band in the 160 KB ring");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;

@@ -256,6 +256,19 @@ def test_paired_k_rows_tile_integer_exact(tile, K):
                                  sizes, tp, rank)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(yb), oracle.column_linear(x, w_r, bias_r, sizes, tp, rank))
+    # LOGICAL layout, bf16 with and without GELU: segment ends (150, 188) cut eight-column chunks, and
+    # an odd row pitch leaves most rows misaligned for 16-byte stores
+    ldy = sum(sizes) + 23
+    for act in (tt.TP_ACT_NONE, tt.TP_ACT_GELU_ERF):
+        ybuf = torch.full((M, ldy), -7.0, dtype=torch.bfloat16, device="cuda")
+        tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, tp, rank, act=act, y=ybuf,
+                            layout=tt.TP_LAYOUT_LOGICAL, ldy=ldy)
+        torch.cuda.synchronize()
+        want, mask = oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=act, layout=oracle.LAYOUT_LOGICAL)
+        got = host_bits(ybuf)
+        sentinel = host_bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0]
+        assert np.array_equal(got[:, :sum(sizes)][:, mask], want[:, mask])
+        assert np.all(got[:, :sum(sizes)][:, ~mask] == sentinel) and np.all(got[:, sum(sizes):] == sentinel)
 
     # the float32 output stage with accumulate on the same tile: a tp = 2 row-parallel pair whose
     # second rank adds onto the first's partial, bit for bit the rank-ordered sum
