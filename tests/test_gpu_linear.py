@@ -301,3 +301,87 @@ def test_64x64_ring_unrolled_loop_integer_exact(K):
     torch.cuda.synchronize()
     assert np.array_equal(host_f32(y), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, out_dtype=oracle.OUT_F32))
     assert np.array_equal(host_bits(yb), oracle.column_linear(x, w_r, b_r, sizes, tp, rank))
+
+
+def _special_inputs(M, K, N, seed):
+    """Integer-valued bf16 x and W (every finite sum exact) with IEEE special values in a few rows:
+    row 0 +inf, row 1 -inf, row 2 NaN, row 3 +inf and -inf (inf - inf where both products meet),
+    row 4 one product that overflows float32 (2^100 * 2^30); W's column 5 is zero for every
+    third output (inf * 0 = NaN there)."""
+    x = synth.bf16_integers((M, K), -3, 3, seed)
+    w = synth.bf16_integers((N, K), -3, 3, seed + 1)
+    w[::3, 5] = 0
+    w[1::3, 5] = 0x3F80  # 1.0: nonzero where the inf lands
+    w[2::3, 5] = 0xBF80  # -1.0
+    w[:, 9] = 0x3F80
+    w[:, 17] = 0x4E80  # 2^30
+    x[0, 5] = 0x7F80      # +inf
+    x[1, 5] = 0xFF80      # -inf
+    x[2, 11] = 0x7FC0     # NaN
+    x[3, 5], x[3, 9] = 0x7F80, 0xFF80
+    x[:, 17] = 0          # the 2^30 column feeds row 4 only: every other sum stays exact in float32
+    x[4, 17] = 0x7180     # 2^100
+    return x, w
+
+
+def _assert_special(got, want, what, finite_close=False):
+    """NaN where the oracle has NaN (any NaN pattern is a correct result) and equal values
+    elsewhere: infinities with their signs always, finite values bit for bit, or within the float
+    tolerance with ``finite_close`` (float32 GELU: float32 erfc against the oracle's float64)."""
+    if got.dtype == np.uint16:
+        gnan = ((got & 0x7F80) == 0x7F80) & ((got & 0x007F) != 0)
+        wnan = ((want & 0x7F80) == 0x7F80) & ((want & 0x007F) != 0)
+    else:
+        gnan, wnan = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gnan, wnan), f"{what}: NaN positions differ"
+    if not finite_close:
+        assert np.array_equal(got[~wnan], want[~wnan]), f"{what}: values differ"
+        return
+    g, w = got[~wnan], want[~wnan]
+    winf = np.isinf(w)
+    assert np.array_equal(g[winf], w[winf]), f"{what}: infinities differ"
+    assert_close(g[~winf], w[~winf], what=what)
+
+
+@pytest.mark.parametrize("tile", [-1, 0, 2, 6])
+def test_column_linear_special_values(tile):
+    """IEEE special values through the column GEMM and every output stage (bf16, bf16 + GELU,
+    float32): infinities, NaN, inf - inf, inf * 0 and a float32 overflow, against the oracle's
+    float64 arithmetic and its rounding (GELU of -inf is NaN on both sides: -inf * erfc(inf))."""
+    tt.set_gemm_tile(tile)
+    M, K, sizes, tp, rank = 130, 128, [300, 76, 76], 2, 1
+    n_r = sum(oracle.shard_widths(sizes, tp, rank)[0])
+    x, w_r = _special_inputs(M, K, n_r, 90)
+    b_r = synth.bf16_integers((n_r,), -8, 8, 93)
+    X, W, B = dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r)
+    with np.errstate(invalid="ignore", over="ignore"):
+        for act in (tt.TP_ACT_NONE, tt.TP_ACT_GELU_ERF):
+            y = tt.tp_column_linear(X, W, B, sizes, tp, rank, act=act)
+            yf = tt.tp_column_linear(X, W, B, sizes, tp, rank, act=act, y_dtype=tt.TP_DTYPE_F32)
+            torch.cuda.synchronize()
+            _assert_special(host_bits(y), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=act),
+                            f"tile {tile} act {act} bf16")
+            _assert_special(host_f32(yf), oracle.column_linear(x, w_r, b_r, sizes, tp, rank, act=act,
+                                                               out_dtype=oracle.OUT_F32), f"tile {tile} act {act} f32",
+                            finite_close=act == tt.TP_ACT_GELU_ERF)
+
+
+@pytest.mark.parametrize("tile", [-1, 0, 6])
+def test_row_partial_special_values_accumulate(tile):
+    """The float32 partial with accumulate on special values: rank 1 adds onto rank 0's partial
+    (inf + finite, inf + NaN, inf - inf across the two ranks)."""
+    tt.set_gemm_tile(tile)
+    M, Kl, N = 130, 256, 200
+    x, w = _special_inputs(M, Kl, N, 95)
+    x[5, 130], x[6, 131] = 0x7F80, 0xFF80  # rank 1's columns: +inf and -inf rows of their own
+    x[0, 140] = 0xFF80                      # row 0: +inf on rank 0, -inf on rank 1
+    S = torch.full((M, N), 5.0, dtype=torch.float32, device="cuda")
+    parts = []
+    with np.errstate(invalid="ignore", over="ignore"):
+        for r in range(2):
+            cols = oracle.shard_rows([Kl], 2, r)
+            xs, ws = np.ascontiguousarray(x[:, cols]), oracle.take_row_shard(w, 2, r)
+            tt.tp_row_linear_partial(dev_bf16(xs), Kl, dev_bf16(ws), None, 2, r, y_partial=S, accumulate=r)
+            parts.append(oracle.row_linear_partial(xs, ws, None, rank=r))
+        torch.cuda.synchronize()
+        _assert_special(host_f32(S), oracle.rank_ordered_sum(parts), f"tile {tile} accumulate")
