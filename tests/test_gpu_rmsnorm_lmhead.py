@@ -53,6 +53,41 @@ def test_rmsnorm_special_rows():
     assert np.all(host_bits(xn)[0] == 0)
 
 
+@pytest.mark.parametrize("scaled", [False, True])
+def test_rmsnorm_extreme_rows(scaled):
+    """Rows whose squares overflow float32 (2^70, 2^100 and the largest finite bf16 next to
+    ordinary values), an infinity, a NaN and a zero row: the factor r (read from the workspace)
+    equals the oracle's float64 factor rounded once, bit for bit, and so do the normalised rows
+    (NaN wherever the oracle has NaN: inf * 0 and NaN propagate)."""
+    K = 512
+    g = np.random.default_rng(9)
+    x = synth.bf16_from_float(g.standard_normal((8, K)))
+    x[0] = 0x6080                                        # every value 2^66: x^2 = 2^132
+    x[1, 3] = 0x7180                                     # one 2^100 among N(0, 1) values
+    x[2, ::2] = 0x7F7F                                   # the largest finite bf16 on every other column
+    x[3, 10] = 0x7F80                                    # +inf: mean square inf, r = 0
+    x[4, 20] = 0x7FC0                                    # NaN
+    x[5] = 0                                             # r = f32(1 / sqrt(eps))
+    x[6] = 0x0001                                        # the smallest bf16 subnormal everywhere
+    s = synth.bf16_from_float(g.standard_normal(K) * 0.1) if scaled else None
+    w = synth.bf16_integers((64, K), -2, 2, 4)
+    M = x.shape[0]
+    ws = torch.zeros(tt.tp_rmsnorm_workspace_bytes(M, K), dtype=torch.uint8, device="cuda")
+    xn = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    tt.rmsnorm_column_linear(dev_bf16(x), dev_bf16(s) if scaled else None, 1e-6, dev_bf16(w), None, [64], 1, 0,
+                             xnorm_out=xn, workspace=ws)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref, r_ref = oracle.rmsnorm(x, s)
+    r_gpu = ws[:M * 4].cpu().numpy().view(np.float32)
+    assert np.array_equal(r_gpu.view(np.uint32), r_ref.view(np.uint32)), (r_gpu, r_ref)
+    got = host_bits(xn)
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_r)
+    assert np.array_equal(got[~nan_r], ref[~nan_r])
+
+
 def _lm_case(B, K, vocab, tp, rank, chunk, seed, fp8):
     rows, off = oracle.vocab_shard(vocab, tp, rank)
     x = synth.bf16_normal((B, K), 1.0, 700 + seed, 0)
