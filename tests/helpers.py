@@ -251,12 +251,14 @@ def check_swiglu(gpu_bits, ref_bits, gate_v, value_v, gate_sums, value_sums, c=C
 
 def check_rmsnorm_rows(xn_gpu, x, s, r0=0):
     """The GPU's normalised rows equal the oracle's, except rows whose factor r took the other
-    admissible float32 rounding: the GPU sums the squares in float32 pieces of K / 256 values
-    (relative error below (K / 256) 2^-24 on the mean square, half that on the factor), so a
-    float32 value that close to the exact factor may be its r. Returns ``(oracle rows, {row: r})``
-    for the rows that took another admissible value."""
+    float32 rounding where that is admissible. The GPU sums the exact squares in float64 (K / 256
+    values per thread, then a tree), then divides, adds eps, takes the square root and the
+    reciprocal in float64: its unrounded factor is within (K / 512 + 8) 2^-53 of the exact one
+    (relative), and the oracle's float64 factor within (log2 K + 4) 2^-53. So the other rounding
+    is admissible only when the oracle's factor lies within (K / 256 + 32) 2^-53 of the midpoint
+    between the two float32 values. Returns ``(oracle rows, {row: r})`` for the rows that took it."""
     ref, r_o = oracle.rmsnorm(x, s)
-    window = (x.shape[1] / 256 + 2) * 2.0 ** -24
+    err = (x.shape[1] / 256 + 32) * 2.0 ** -53
     bad = np.nonzero(np.any(xn_gpu != ref, axis=1))[0]
     other = {}
     if bad.size:
@@ -266,7 +268,8 @@ def check_rmsnorm_rows(xn_gpu, x, s, r0=0):
             for dr in (-1, 1):
                 cand = np.array([np.nextafter(r_o[b], np.float32(np.inf) if dr > 0 else np.float32(-np.inf))],
                                 dtype=np.float32)
-                if abs(float(cand[0]) - rho[i]) > window * rho[i]:
+                mid = (float(cand[0]) + float(r_o[b])) / 2.0
+                if abs(mid - rho[i]) > err * rho[i]:
                     continue
                 y, _ = oracle.rmsnorm(x[b:b + 1], s, r=cand)
                 if np.array_equal(y[0], xn_gpu[b]):
