@@ -280,7 +280,8 @@ TP_API size_t tp_rmsnorm_workspace_min_bytes(int64_t M, int64_t K);
  * (the T5X option that centres the learned scale at zero), so t = bf16(1 + s) and y = bf16(n * t).
  * transformer_layer_weight_gathered normalises without a scale (scale = NULL).
  * One device holds whole rows, so the page's mean across shards is the mean of
- * the row.
+ * the row. The library sums the exact squares in float64 and rounds r to float32
+ * once (at least the page's float32 precision; no finite row overflows).
  *
  * x          device bf16 [M, K]
  * scale      device bf16 [K] or NULL
