@@ -25,6 +25,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
+// exp(y) for finite y in float32: y log2 e is split into h + l (log2 e as two floats, the
+// product's error from an fma) and 2^(h + l) = 2^h (1 + l ln 2), with the hardware exp2 for 2^h,
+// so the rounding of y log2 e is not amplified for large |y|.
+__device__ __forceinline__ float exp_split(float y) {
+  constexpr float kL2eHi = 1.44269502162933349609375f;  // log2 e, leading float
+  constexpr float kL2eLo = 1.92596299e-8f;               // log2 e - kL2eHi
+  const float h = y * kL2eHi;
+  const float l = fmaf(y, kL2eLo, fmaf(y, kL2eHi, -h));  // y log2 e = h + l
+  const float e2 = __builtin_amdgcn_exp2f(h);
+  return fmaf(e2, l * 0.69314718055994531f, e2);
+}
+
 // Exact (erf) GELU in float32: 0.5 a (1 + erf(a / sqrt 2)), evaluated as 0.5 a erfc(-a / sqrt 2)
 // (the same function) so that large negative inputs keep their relative accuracy instead of
 // cancelling in 1 + erf. erfc(z), z = |a| / sqrt 2, is the Chebyshev-fitted approximation erfcc
@@ -33,8 +45,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // 2 - erfc(z) for a > 0. Two steps keep float32 evaluation close to that bound:
 // - the exponent takes z^2 as a^2 / 2 from the exact split a^2 = s + e (s rounded, e = fma(a, a,
 //   -s)), so the rounding of a / sqrt 2 is not amplified by exp;
-// - exp(y) = 2^(y log2 e): the product y log2 e is split into h + l (log2 e as two floats, the
-//   product's error from an fma) and 2^(h + l) = 2^h (1 + l ln 2), with the hardware exp2 for 2^h.
+// - exp(y) from exp_split.
 // z stops at 13, where erfc underflows float32 (larger |a| would overflow the square).
 // Measured against float64 erf-GELU in a float32 emulation of these steps, every finite bf16
 // input rounds to the same bf16 output; the largest errors are about 6 float32 ulps for
@@ -59,21 +70,26 @@ __device__ __forceinline__ float gelu_erf(float a) {
   const float sq = ac * ac;
   const float sq_err = fmaf(ac, ac, -sq);  // a^2 = sq + sq_err exactly
   const float y = fmaf(-0.5f, sq_err, fmaf(-0.5f, sq, p));
-  constexpr float kL2eHi = 1.44269502162933349609375f;           // log2 e, leading float
-  constexpr float kL2eLo = 1.92596299e-8f;                        // log2 e - kL2eHi
-  const float h = y * kL2eHi;
-  const float l = fmaf(y, kL2eLo, fmaf(y, kL2eHi, -h));          // y log2 e = h + l
-  const float e2 = __builtin_amdgcn_exp2f(h);
-  const float q = t * fmaf(e2, l * 0.69314718055994531f, e2);     // erfc(z)
+  const float q = t * exp_split(y);  // erfc(z)
   return 0.5f * a * (a < 0.0f ? q : 2.0f - q);
 }
 
 // SwiGLU of one output from float32 accumulators: the gate and the value are rounded to bf16
-// first, then Swish with unit slope, g / (1 + exp(-g)), times the value, in float32. For
-// g < -88.7 exp(-g) is inf and the Swish is -0, its limit.
+// first, then Swish with unit slope, g / (1 + exp(-g)), times the value, in float32. For very
+// negative g the Swish underflows (a subnormal, or -0 below about -104), as float64 rounded to
+// float32 does.
 __device__ __forceinline__ float swiglu_of(float gate, float value) {
   const float g = bf16_to_f32(f32_to_bf16(gate)), u = bf16_to_f32(f32_to_bf16(value));
-  return g / (1.0f + expf(-g)) * u;
+  // swish(g) = g / (1 + exp(-g)) from E = exp(-|g|) in (0, 1], so nothing overflows: g / (1 + E)
+  // for g >= 0, g E / (1 + E) for g < 0 (E is exactly 0 below -150, where -inf gives NaN as
+  // -inf / (1 + inf) does). The reciprocal of 1 + E, in (1, 2], is the hardware estimate plus one
+  // Newton step. In a float32 emulation the Swish of every finite bf16 gate is within 2.3 ulp of
+  // float64 (the correctly rounded library exp and divide: 1.8).
+  const float e = exp_split(fmaxf(-fabsf(g), -150.0f));
+  const float d = 1.0f + e;
+  float r = __builtin_amdgcn_rcpf(d);
+  r = fmaf(r, fmaf(-d, r, 1.0f), r);
+  return (g < 0.0f ? (g * e) * r : g * r) * u;
 }
 
 // Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>). Register arrays indexed
