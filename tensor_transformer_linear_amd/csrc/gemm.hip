@@ -244,7 +244,18 @@ __device__ __forceinline__ void gemm_store_tile_bf16(const GemmProblem& p, f32x1
       for (int e = 0; e < 8 && col + e < N; ++e) out[col + e + seg_of(ep, col + e, {hit.delta, 0}).delta] = src[e];
     }
   };
-  if constexpr (PASS == FM) {
+  if constexpr (PASS == FM && GELU) {
+    // GELU makes parking vector-ALU bound: band i + 1 is parked while band i drains, so the
+    // drain's LDS reads and stores overlap the next band's arithmetic (one barrier per band)
+    park(std::integral_constant<int, 0>{}, 0);
+    __syncthreads();
+    static_for<FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 1 < FM) park(std::integral_constant<int, i + 1>{}, i + 1);
+      if (drain(i, i)) drain_partial(i, i);
+      if constexpr (i + 1 < FM) __syncthreads();
+    });
+  } else if constexpr (PASS == FM) {
     static_for<FM>([&](auto i) { park(i, decltype(i)::value); });
     __syncthreads();
     bool partial = false;
