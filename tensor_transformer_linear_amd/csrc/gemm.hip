@@ -933,7 +933,7 @@ constexpr int pair_wait(int from, int to, int parity, int ra, int rb) {
   return n;
 }
 
-template <int BM, int BN, int SLOTS, bool FP8, bool MAPPED, int EPI = EPI_GENERIC>
+template <int BM, int BN, int SLOTS, bool FP8, bool MAPPED, int EPI = EPI_GENERIC, bool PP = false>
 __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int tiles_m, int tiles_n, int group_m) {
   constexpr int WAVES_M = 2, WAVES_N = 4, WM = BM / 2, WN = BN / 4, FM = WM / 32, FN = WN / 32;
   constexpr int HALF = (BM > BN ? BM : BN) * 128;  // slot size: the larger operand's half
@@ -1103,13 +1103,49 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   auto next = [](unsigned v, unsigned d) { return v + d >= SLOTS ? v + d - SLOTS : v + d; };
   constexpr int H0 = SLOTS - 2;  // half issued at the first step of pair 0
   int j = 0;
-  for (; 2 * j + SLOTS <= 2 * np; ++j) {
+  if constexpr (PP) {
+    // PP: one memory phase and one compute phase per K pair instead of per K step (the
+    // 128x128 tile, whose four MFMAs per step are too few to cover a step's memory phase).
+    // Pair j reads all four fragment sets of the pair, issues halves 2j + S - 2 and 2j + S - 1
+    // (into pair j - 1's slots, which both groups finished reading one barrier earlier) and
+    // waits until pair j + 1 has landed (the halves issued after it: 2j + 4 .. 2j + S - 1).
+    static_assert(!FP8, "pair phases: bf16 only");
+    constexpr int VM_PAIR = pair_wait(4, SLOTS - 1, 0, RA, RB);
+    static_assert(VM_PAIR < 64, "vmcnt immediate is six bits");
+    Frag f2, f3;
+    auto pair_phase = [&](unsigned sa_, unsigned sb_, int h0, int h1) {
+      read(f0, sa_, sb_, 0, 0);
+      read(f1, sa_, sb_, 0, 1);
+      read(f2, sa_, sb_, 1, 0);
+      read(f3, sa_, sb_, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int c0 = h0 < 2 * np ? h0 : 2 * (np - 1) + (h0 & 1);
+      const int c1 = h1 < 2 * np ? h1 : 2 * (np - 1) + (h1 & 1);
+      issue_half(c0 >> 1, c0 & 1, (unsigned)c0 % SLOTS);
+      issue_half(c1 >> 1, c1 & 1, (unsigned)c1 % SLOTS);
+      wait_barrier(std::integral_constant<int, VM_PAIR>{}, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_s_setprio(1);
+      mma(f0);
+      mma(f1);
+      mma(f2);
+      mma(f3);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (; j < np; ++j) {
+      pair_phase(sa, sa + 1 == SLOTS ? 0 : sa + 1, 2 * j + H0, 2 * j + H0 + 1);
+      sa = next(sa, 2);
+    }
+  }
+  for (; !PP && 2 * j + SLOTS <= 2 * np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
     step(sa, sb, 0, j + (H0 >> 1), H0 & 1, next(sa, SLOTS - 2), std::integral_constant<int, VM_EVEN>{});
     step(sa, sb, 1, j + ((H0 + 1) >> 1), (H0 + 1) & 1, next(sa, SLOTS - 1), std::integral_constant<int, VM_ODD>{});
     sa = next(sa, 2);
   }
-  for (; j < np; ++j) {
+  for (; !PP && j < np; ++j) {
     const unsigned sb = sa + 1 == SLOTS ? 0 : sa + 1;
     int h = 2 * j + H0, hc = h < 2 * np ? h : 2 * (np - 1) + (h & 1);
     step(sa, sb, 0, hc >> 1, hc & 1, (unsigned)hc % SLOTS, std::integral_constant<int, VM_EVEN>{});
@@ -1171,21 +1207,22 @@ hipError_t launch_tile(const GemmProblem& p, int path, hipStream_t stream) {
     if constexpr ((BM == 256 || BM == 128) && (BN == 256 || BN == 128) && WAVES_M == 2 && WAVES_N == 4 &&
                   SCHED == 1) {
       constexpr int S = BM == 256 || BN == 256 ? 5 : 10;  // 160 KB of halves
+      constexpr bool PP = BM == 128 && BN == 128;         // one phase per K pair (see the kernel)
       if (p.K % 64 == 0) {                               // whole K pairs: 128-byte LDS rows
         if (mapped)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, true>), grid, block, 0, stream, p, tiles_m,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, true, EPI_GENERIC, PP>), grid, block, 0, stream, p, tiles_m,
                              tiles_n, group_m);
         else if (epilogue_mode(p.ep) == EPI_BF16)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16>), grid, block, 0, stream, p,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16, PP>), grid, block, 0, stream, p,
                              tiles_m, tiles_n, group_m);
         else if (epilogue_mode(p.ep) == EPI_BF16_GELU)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16_GELU>), grid, block, 0, stream,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_BF16_GELU, PP>), grid, block, 0, stream,
                              p, tiles_m, tiles_n, group_m);
         else if (epilogue_mode(p.ep) == EPI_F32)
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_F32>), grid, block, 0, stream, p,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_F32, PP>), grid, block, 0, stream, p,
                              tiles_m, tiles_n, group_m);
         else
-          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false>), grid, block, 0, stream, p, tiles_m,
+          hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, S, false, false, EPI_GENERIC, PP>), grid, block, 0, stream, p, tiles_m,
                              tiles_n, group_m);
         return hipGetLastError();
       }
