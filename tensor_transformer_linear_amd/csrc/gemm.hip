@@ -1289,18 +1289,31 @@ hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
 
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
-  const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= 192) return TILE_256x256;  // the 8-wave 256x256 tile wins even with a partial last wave
-  if (N % 224 == 0 && (long long)((M + 255) / 256) * (N / 224) >= 256) return TILE_256x224;
-  const long long t256x128 = (long long)((M + 255) / 256) * ((N + 127) / 128);
-  if (t256x128 >= 256) {
-    // at the same tile count 128x256 measured 4-5% ahead of 256x128 (4096x2048x4096: 68.6 against
-    // 72.3 us; 8192x1024x8192: 121.4 against 126.7 us)
-    const long long t128x256 = (long long)((M + 127) / 128) * ((N + 255) / 256);
-    return t128x256 <= t256x128 ? TILE_128x256 : TILE_256x128;
+  auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  // One workgroup per CU and 256 CUs: a launch runs floor(tiles / 256) full waves and maybe a
+  // partial one. Wave times at K = 4096 with every CU busy: 256x256 105 us, 128x256 64,
+  // 256x128 65.6, 128x128 39.2 (relative 100, 61, 62.5, 37.3). A partial wave of r tiles runs
+  // at a higher clock and takes about 0.62 + 0.38 r / 256 of a full one (256x256: 48 tiles
+  // 67-68 us, 96 tiles 73-75, 128 tiles 82, 224 tiles 96). The least modelled time wins, the
+  // larger tile at a tie: 6144x1536x4096 77.9 us on 144 256x256 tiles against 105.9 on 288
+  // 128x256 tiles; 2048x3072x4096 56.2 us on 192 256x128 tiles against 69.3 on 384 128x128.
+  const long long t128 = tiles(128, 128);
+  if (t128 >= 128) {
+    const struct {
+      int tile;
+      long long n;
+      double wave;
+    } c[] = {{TILE_256x256, tiles(256, 256), 100.0}, {TILE_128x256, tiles(128, 256), 61.0},
+             {TILE_256x128, tiles(256, 128), 62.5}, {TILE_128x128, t128, 37.3}};
+    int best = 0;
+    double best_t = 0.0;
+    for (int i = 0; i < 4; ++i) {
+      const long long full = c[i].n / 256, r = c[i].n % 256;
+      const double t = c[i].wave * ((double)full + (r ? 0.62 + 0.38 * (double)r / 256.0 : 0.0));
+      if (i == 0 || t < best_t) best = i, best_t = t;
+    }
+    return c[best].tile;
   }
-  const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
-  if (t128 >= 128) return TILE_128x128;
   // below a full wave of 128x64 tiles the K loop's latency decides: 64x64 tiles keep twice as
   // many CUs busy (1024x512x4096: 21 us against 35 us; 2048x768x4096: 36 against 38)
   if ((long long)((M + 127) / 128) * ((N + 63) / 64) >= 256) return TILE_128x64;
