@@ -217,6 +217,21 @@ def test_tuning_choices_checked_before_anything_else():
     assert tt.gemm_pick_tile(32768, 3072, 8192) in tt.GEMM_TILES
 
 
+@pytest.mark.parametrize("M, N, want", [
+    (32768, 3072, "256x256"), (8192, 1792, "256x256"), (8192, 4096, "256x256"),  # workload GEMMs
+    (4096, 768, "128x128"), (256, 1536, "64x64"), (256, 768, "64x64"),
+    (4096, 2048, "128x256"),   # 256 tiles: one full wave
+    (2048, 3072, "128x256"),   # 192 tiles against 384 128x128 tiles (two waves)
+    (6144, 1536, "256x256"),   # 144 tiles in one wave against 288 128x256 tiles
+    (4096, 4608, "128x256"),   # 576 128x256 tiles against 1.125 waves of 256x256 tiles
+    (1024, 512, "64x64"),
+])
+def test_gemm_tile_picker_choices(M, N, want):
+    # the picker's modelled wave times (one workgroup per CU, 256 CUs, partial waves cheaper)
+    bm, bn = tt.GEMM_TILES[tt.gemm_pick_tile(M, N, 4096)]
+    assert f"{bm}x{bn}" == want
+
+
 def test_stream_probe_host_checks():
     # refused on the host before any launch (no GPU needed)
     T = tt.tuning_lib()
