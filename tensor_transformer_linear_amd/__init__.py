@@ -82,6 +82,7 @@ def _tuning_name(name: str) -> str:
 TUNING_SIGNATURES = {
     **{_tuning_name(n): (SIGNATURES[n][0], SIGNATURES[n][1] + [_int] * len(c)) for n, c in TUNING_CHOICES.items()},
     "tpt_gemm_pick_tile": (_int, [_i64, _i64, _i64]),
+    "tpt_gemm_fp8_pick_tile": (_int, [_i64, _i64, _i64]),
     "tpt_lm_head_shape_count": (_int, []),
     "tpt_mfma_row_sums": (_int, [_int, _vp, _vp, _vp, _vp]),
     "tpt_stream_probe": (_int, [_int, _int, _vp, _i64, _vp, _vp]),
@@ -554,6 +555,11 @@ LM_HEAD_SHAPES = {0: (4, 8, 8, 1), 1: (2, 8, 8, 1), 2: (4, 4, 8, 1), 3: (2, 4, 8
 def gemm_pick_tile(M: int, N: int, K: int) -> int:
     """The tile the library picks for an M x N x K bf16 GEMM (a key of ``GEMM_TILES``; -1 if invalid)."""
     return int(tuning_lib().tpt_gemm_pick_tile(M, N, K))
+
+
+def gemm_fp8_pick_tile(M: int, N: int, K: int) -> int:
+    """The tile the library picks for an M x N x K E4M3 GEMM (0 or 2, keys of ``GEMM_TILES``; -1 if invalid)."""
+    return int(tuning_lib().tpt_gemm_fp8_pick_tile(M, N, K))
 
 
 GEMM_TILES = {0: (256, 256), 1: (256, 128), 2: (128, 128), 3: (128, 256), 4: (256, 224), 5: (128, 64), 6: (64, 64)}

@@ -1105,11 +1105,11 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
   int j = 0;
   if constexpr (PP) {
     // PP: one memory phase and one compute phase per K pair instead of per K step (the
-    // 128x128 tile, whose four MFMAs per step are too few to cover a step's memory phase).
+    // 128x128 tile, whose few MFMAs per step, four bf16 or two fp8, cannot cover a step's
+    // memory phase).
     // Pair j reads all four fragment sets of the pair, issues halves 2j + S - 2 and 2j + S - 1
     // (into pair j - 1's slots, which both groups finished reading one barrier earlier) and
     // waits until pair j + 1 has landed (the halves issued after it: 2j + 4 .. 2j + S - 1).
-    static_assert(!FP8, "pair phases: bf16 only");
     constexpr int VM_PAIR = pair_wait(4, SLOTS - 1, 0, RA, RB);
     static_assert(VM_PAIR < 64, "vmcnt immediate is six bits");
     Frag f2, f3;
@@ -1125,10 +1125,15 @@ __global__ __launch_bounds__(512) void gemm_nt_pair_kernel(GemmProblem p, int ti
       issue_half(c1 >> 1, c1 & 1, (unsigned)c1 % SLOTS);
       wait_barrier(std::integral_constant<int, VM_PAIR>{}, std::integral_constant<int, 0>{});
       __builtin_amdgcn_s_setprio(1);
-      mma(f0);
-      mma(f1);
-      mma(f2);
-      mma(f3);
+      if constexpr (FP8) {
+        mma8(f0, f1);
+        mma8(f2, f3);
+      } else {
+        mma(f0);
+        mma(f1);
+        mma(f2);
+        mma(f3);
+      }
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
@@ -1253,12 +1258,13 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
   static_assert(tile_uses_buffer_loads<BM, BN, 8>(), "the fp8 tiles load through buffer resources");
   if (!buffer_span_ok(p, BM, BN)) return hipErrorNotSupported;
   if (p.K % 128 == 0) {  // whole K pairs: 128-byte LDS rows
+    constexpr bool PP = BM == 128;  // one phase per K pair (see the kernel)
     if (epilogue_mode(p.ep) == EPI_FP8_BF16)
-      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false, EPI_FP8_BF16>),
+      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false, EPI_FP8_BF16, PP>),
                          dim3(tiles_m * tiles_n), dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
     else
-      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false>), dim3(tiles_m * tiles_n),
-                         dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
+      hipLaunchKernelGGL((gemm_nt_pair_kernel<BM, BN, BM == 256 ? 5 : 10, true, false, EPI_GENERIC, PP>),
+                         dim3(tiles_m * tiles_n), dim3(512), 0, stream, p, tiles_m, tiles_n, group_m);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((gemm_nt_dma_kernel<BM, BN, 2, 4, 4, 1, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, p,
@@ -1268,10 +1274,25 @@ hipError_t launch_tile_fp8(const GemmProblem& p, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+// A launch's modelled time in full-wave units: one workgroup per CU and 256 CUs give
+// floor(n / 256) full waves, and r left-over tiles a partial wave that runs at a higher clock
+// (power cap) and takes part0 + (1 - part0) r / 256 of a full one.
+double wave_units(long long n, double part0) {
+  const long long r = n % 256;
+  return (double)(n / 256) + (r ? part0 + (1.0 - part0) * (double)r / 256.0 : 0.0);
+}
+}  // namespace
+
 int gemm_fp8_pick_tile(int M, int N, int K) {
   (void)K;
+  // Full-wave times at K = 4096: 256x256 58.9 us, 128x128 24.7 (relative 100, 42); a partial
+  // wave costs 0.72 + 0.28 r / 256 of a full one (256x256: 48 tiles 43.9 us, 128 tiles 47.4).
+  // 6144x1536x4096: 48.0 us on 144 256x256 tiles against 60.7 on 576 128x128 tiles;
+  // 2048x3072x4096: 41.5 us on 384 128x128 tiles against 45.9 on 96 256x256 tiles.
   const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 192 ? TILE_256x256 : TILE_128x128;
+  const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  return 100.0 * wave_units(t256, 0.72) <= 42.0 * wave_units(t128, 0.72) ? TILE_256x256 : TILE_128x128;
 }
 
 hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
@@ -1290,13 +1311,12 @@ hipError_t launch_gemm_fp8(const GemmProblem& p, int tile, hipStream_t stream) {
 int gemm_pick_tile(int M, int N, int K) {
   (void)K;
   auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  // One workgroup per CU and 256 CUs: a launch runs floor(tiles / 256) full waves and maybe a
-  // partial one. Wave times at K = 4096 with every CU busy: 256x256 105 us, 128x256 64,
-  // 256x128 65.6, 128x128 39.2 (relative 100, 61, 62.5, 37.3). A partial wave of r tiles runs
-  // at a higher clock and takes about 0.62 + 0.38 r / 256 of a full one (256x256: 48 tiles
-  // 67-68 us, 96 tiles 73-75, 128 tiles 82, 224 tiles 96). The least modelled time wins, the
-  // larger tile at a tie: 6144x1536x4096 77.9 us on 144 256x256 tiles against 105.9 on 288
-  // 128x256 tiles; 2048x3072x4096 56.2 us on 192 256x128 tiles against 69.3 on 384 128x128.
+  // Full-wave times at K = 4096: 256x256 105 us, 128x256 64, 256x128 65.6, 128x128 39.2
+  // (relative 100, 61, 62.5, 37.3); a partial wave costs 0.62 + 0.38 r / 256 of a full one
+  // (256x256: 48 tiles 67-68 us, 96 tiles 73-75, 128 tiles 82, 224 tiles 96). The least
+  // modelled time wins, the larger tile at a tie: 6144x1536x4096 77.9 us on 144 256x256 tiles
+  // against 105.9 on 288 128x256 tiles; 2048x3072x4096 56.2 us on 192 256x128 tiles against
+  // 69.3 on 384 128x128.
   const long long t128 = tiles(128, 128);
   if (t128 >= 128) {
     const struct {
@@ -1308,8 +1328,7 @@ int gemm_pick_tile(int M, int N, int K) {
     int best = 0;
     double best_t = 0.0;
     for (int i = 0; i < 4; ++i) {
-      const long long full = c[i].n / 256, r = c[i].n % 256;
-      const double t = c[i].wave * ((double)full + (r ? 0.62 + 0.38 * (double)r / 256.0 : 0.0));
+      const double t = c[i].wave * wave_units(c[i].n, 0.62);
       if (i == 0 || t < best_t) best = i, best_t = t;
     }
     return c[best].tile;

@@ -51,9 +51,10 @@ TP_API int tpt_lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t
                                     const float* w_block_scale, float* logits, int32_t* argmax_local,
                                     float* max_logit, void* workspace, size_t workspace_bytes, void* stream,
                                     int lm_shape);
-/* The automatic tile for an M x N x K bf16 GEMM (-1 for invalid sizes), and the number of
- * LM-head launch shapes. */
+/* The automatic tile for an M x N x K bf16 GEMM and for an E4M3 one (-1 for invalid sizes),
+ * and the number of LM-head launch shapes. */
 TP_API int tpt_gemm_pick_tile(int64_t M, int64_t N, int64_t K);
+TP_API int tpt_gemm_fp8_pick_tile(int64_t M, int64_t N, int64_t K);
 TP_API int tpt_lm_head_shape_count(void);
 
 /* One matrix instruction on fixed operands, to observe its rounding: A holds 32 rows (fp8 = 0:

@@ -92,6 +92,11 @@ TP_API int tpt_gemm_pick_tile(int64_t M, int64_t N, int64_t K) {
   return tpk::gemm_pick_tile((int)M, (int)N, (int)K);
 }
 
+TP_API int tpt_gemm_fp8_pick_tile(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return -1;
+  return tpk::gemm_fp8_pick_tile((int)M, (int)N, (int)K);
+}
+
 TP_API int tpt_lm_head_shape_count(void) { return tpk::lm_head_shape_count(); }
 
 }  // extern "C"

@@ -232,6 +232,18 @@ def test_gemm_tile_picker_choices(M, N, want):
     assert f"{bm}x{bn}" == want
 
 
+@pytest.mark.parametrize("M, N, want", [
+    (32768, 3072, "256x256"), (4096, 4096, "256x256"), (4096, 768, "128x128"),
+    (6144, 1536, "256x256"),   # 144 tiles in one wave against 576 128x128 tiles
+    (2048, 3072, "128x128"),   # 384 128x128 tiles against 96 256x256 tiles
+    (4096, 2048, "128x128"),
+])
+def test_gemm_fp8_tile_picker_choices(M, N, want):
+    bm, bn = tt.GEMM_TILES[tt.gemm_fp8_pick_tile(M, N, 4096)]
+    assert f"{bm}x{bn}" == want
+    assert tt.gemm_fp8_pick_tile(0, 1, 1) == -1
+
+
 def test_stream_probe_host_checks():
     # refused on the host before any launch (no GPU needed)
     T = tt.tuning_lib()
