@@ -164,3 +164,20 @@ def test_fp8_prefill_workload4_shape_every_row():
         n += check_bf16(got[r0:r1], ref, v, sums, c=C_FP8, what=f"fp8 rows {r0}:{r1}", share=FP8_SHARE)
         worst = max(worst, check_f32(got32[r0:r1], v, sums.block(0, r1 - r0), c=C_FP8, what=f"fp8 f32 rows {r0}:{r1}"))
     print(f"fp8 prefill: {n} rounding straddles of {got.size}; largest float32 error / sum|x w| = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,N,want", [(6144, 1536, 0), (2048, 3072, 2), (1024, 8704, 0)])
+def test_fp8_picked_tile_exact_on_integer_codes(M, N, want):
+    """The automatic fp8 tile where the wave-time model decides, exact on integer codes (K = 128)."""
+    assert tt.gemm_fp8_pick_tile(M, N, 128) == want
+    g = np.random.default_rng(M + N)
+    K = 128
+    ints = np.array([-4, -3, -2, -1, 0, 1, 2, 3, 4], np.float32)
+    xq = oracle.e4m3_encode(g.choice(ints, (M, K)))
+    wq = oracle.e4m3_encode(g.choice(ints, (N, K)))
+    xs = (2.0 ** g.integers(-4, 4, M)).astype(np.float32)
+    ws = (2.0 ** g.integers(-4, 4, N)).astype(np.float32)
+    y = tt.tp_column_linear_fp8(dev_u8(xq), dev_f32(xs), dev_u8(wq), dev_f32(ws), None, [N], 1, 0,
+                                y_dtype=tt.TP_DTYPE_F32)
+    ref = oracle.column_linear_fp8(xq, xs, wq, ws, None, [N], 1, 0, out_dtype=oracle.OUT_F32)
+    assert np.array_equal(host_f32(y), ref)

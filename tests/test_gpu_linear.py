@@ -385,3 +385,19 @@ def test_row_partial_special_values_accumulate(tile):
             parts.append(oracle.row_linear_partial(xs, ws, None, rank=r))
         torch.cuda.synchronize()
         _assert_special(host_f32(S), oracle.rank_ordered_sum(parts), f"tile {tile} accumulate")
+
+
+@pytest.mark.parametrize("M,N,want", [(2048, 3072, 3), (6144, 1536, 0), (4096, 4608, 3), (5120, 1024, 3),
+                                      (1024, 9216, 0), (4096, 768, 2)])
+def test_picked_tile_integer_exact(M, N, want):
+    """The automatic tile on shapes where the wave-time model decides (one tile wave more or less
+    than the tile-count rules would give): the launch the picker makes, bit-exact on integer
+    inputs, K = 128 (two K pairs), bias and a ragged last row."""
+    assert tt.gemm_pick_tile(M, N, 128) == want
+    tt.set_gemm_tile(-1)
+    tt.set_gemm_path(-1)
+    M, K, sizes = M - 3, 128, [N]
+    x, w, b, w_r, b_r = _int_inputs(M, K, sizes, 1, 0, 900 + N)
+    y = tt.tp_column_linear(dev_bf16(x), dev_bf16(w_r), dev_bf16(b_r), sizes, 1, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y), oracle.column_linear(x, w_r, b_r, sizes, 1, 0))
