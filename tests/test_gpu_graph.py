@@ -32,6 +32,13 @@ def test_graph_replays_match_eager():
     h_r, fph, qph = oracle.qwi_dims(heads, padded, qkv, ff, tp)
     wq = dev_bf16(synth.bf16_normal((h_r * qph, K), 0.02, 972, 0))
     res = dev_bf16(synth.bf16_normal((M // tp, K), 1.0, 973, 0))
+    # the eight-wave paired-row kernels: 128x128 (one ping-pong phase per K pair) and 256x256
+    big = [(2048, 1024, 256), (4096, 4096, 128)]
+    assert [tt.gemm_pick_tile(m, n, k) for m, n, k in big] == [2, 0]
+    xb = [dev_bf16(synth.bf16_normal((m, k), 1.0, 974, i)) for i, (m, n, k) in enumerate(big)]
+    wb = [dev_bf16(synth.bf16_normal((n, k), 0.02, 975, i)) for i, (m, n, k) in enumerate(big)]
+    bb = [dev_bf16(synth.bf16_normal((n,), 0.1, 976, i)) for i, (m, n, k) in enumerate(big)]
+    yb = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for m, n, k in big]
 
     g_out = [torch.empty((M, inter // tp), dtype=torch.bfloat16, device=dev) for _ in range(tp)]
     part = torch.empty((M, K), dtype=torch.float32, device=dev)
@@ -43,7 +50,7 @@ def test_graph_replays_match_eager():
     ws = tt.lm_head_workspace(B, vocab, 2, 1)
     yf = torch.zeros((M, h_r, qkv + fph), dtype=torch.bfloat16, device=dev)
     q = torch.empty((M, h_r, qkv), dtype=torch.bfloat16, device=dev)
-    outs = g_out + [part, z, lg, am, mx, yf, q] + parts
+    outs = g_out + [part, z, lg, am, mx, yf, q] + parts + yb
 
     def chain():
         for r in range(tp):
@@ -53,6 +60,8 @@ def test_graph_replays_match_eager():
         tt.tp_reduce_scatter_residual(parts, 1, M, 1, residual=res, z=z)
         tt.lm_head_shard_argmax(xh, vocab, 2, 1, chunk, wh, logits=lg, argmax_local=am, max_logit=mx, workspace=ws)
         tt.tp_qwi_swiglu(x, heads, padded, qkv, ff, tp, 0, wq, yf, q=q)
+        for i, (m, n, k) in enumerate(big):
+            tt.tp_column_linear(xb[i], wb[i], bb[i], [n], 1, 0, act=tt.TP_ACT_GELU_ERF if i else tt.TP_ACT_NONE, y=yb[i])
 
     chain()
     torch.cuda.synchronize()
