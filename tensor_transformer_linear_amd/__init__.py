@@ -549,7 +549,8 @@ GEMM_PATH_AUTO, GEMM_PATH_REGISTER, GEMM_PATH_DMA = -1, 0, 1
 LM_HEAD_SHAPES = {0: (4, 8, 8, 1), 1: (2, 8, 8, 1), 2: (4, 4, 8, 1), 3: (2, 4, 8, 1), 4: (4, 8, 4, 1),
                   5: (1, 8, 8, 1), 6: (4, 8, 4, 2), 7: (8, 4, 4, 2), 8: ("lds-ring", 64), 9: ("lds-ring", 128),
                   10: ("x-resident", 64), 11: ("row-quad", 0), 12: ("row-quad", 1), 13: ("row-quad", 2),
-                  14: ("row-quad", 3), 15: ("row-quad", 4)}
+                  14: ("row-quad", 3), 15: ("row-quad", 4),
+                  16: ("row-quad", 5)}
 
 
 def gemm_pick_tile(M: int, N: int, K: int) -> int:

@@ -11,7 +11,7 @@
 // second kernel launched right after reduces (a kernel boundary instead of per-workgroup
 // device-scope fences, which on gfx950 write back and invalidate the whole L2).
 //
-// * Row-quad (shapes 11-15; the default): a workgroup owns 64 rows over the whole K, x sits
+// * Row-quad (shapes 11-16; the default): a workgroup owns 64 rows (128: shape 16) over the whole K, x sits
 //   in LDS one slice at a time (32 or 64 batch rows per pass), and each weight load
 //   instruction reads 4 rows x 256 contiguous bytes into registers; each wave turns its
 //   loads into the MFMA operand layout through 4 KB of its own LDS.
@@ -60,7 +60,7 @@ constexpr LmShape kLmShapes[] = {{4, 8, 8, 1}, {2, 8, 8, 1}, {4, 4, 8, 1}, {2, 4
                                  {4, 8, 4, 1}, {1, 8, 8, 1}, {4, 8, 4, 2}, {8, 4, 4, 2}};
 constexpr int kLmDmaShape = 8;  // 8, 9: the direct-to-LDS kernel (indices past the table)
 constexpr int kLmXresShape = 10;  // the x-resident kernel (batch passes of up to 64 rows)
-constexpr int kLmQuadShape = 11;  // 11 .. 15: the row-quad kernel (batch passes of 32 rows)
+constexpr int kLmQuadShape = 11;  // 11 .. 16: the row-quad kernel (batch passes of 32 or 64 rows)
 constexpr int kLmRingShape = 9;  // LDS ring, 128-byte stages (falls back to 4 for a ragged bf16 K)
 
 // Two E4M3 codes (bytes HI ? 2,3 : 0,1 of w) -> two bf16, exactly (scale 1).
@@ -584,11 +584,11 @@ constexpr int LMX_THREADS = 512;
 // [batch row][tile].
 template <int BH>
 __device__ __forceinline__ void lm_tile64_finish(const LmHeadProblem& p, const f32x4_t (&acc)[BH], float* red,
-                                                 int n_tiles, int b0, int nbatch) {
+                                                 int n_tiles, int b0, int nbatch, int tile) {
   constexpr int BROWS = 16 * BH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = wave & 3, hk = wave >> 2, r16 = lane & 15, q = lane >> 4;
-  const int tile = blockIdx.x, row0 = tile * LMX_ROWS, V = p.V;
+  const int row0 = tile * LMX_ROWS, V = p.V;
   static_for<BH>([&](auto hb) {
     static_for<4>([&](auto v) {
       constexpr int vv = v;
@@ -784,7 +784,7 @@ __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem
   }
 
   // every wave passed the loop's last barrier: the x buffers are free for the reduction
-  lm_tile64_finish<BH>(p, acc, reinterpret_cast<float*>(xs), n_tiles, b0, nbatch);
+  lm_tile64_finish<BH>(p, acc, reinterpret_cast<float*>(xs), n_tiles, b0, nbatch, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -816,21 +816,26 @@ __global__ __launch_bounds__(LMX_THREADS) void lm_head_xres_kernel(LmHeadProblem
 constexpr int lm_gcd(int a, int b) { return b == 0 ? a : lm_gcd(b, a % b); }
 constexpr int lm_lcm(int a, int b) { return a / lm_gcd(a, b) * b; }
 
-template <bool FP8, int XS_K, int BH>
+//
+// RPW = 2: the workgroup owns two 64-row blocks (128 rows) and wave w multiplies row group g in
+// both, rows 16 g and 64 + 16 g of the workgroup's rows, so every x fragment a wave reads from
+// LDS feeds two MFMAs and each workgroup's x slices serve twice the weight bytes. A window is
+// then one 16-row window per block (eight loads); candidates stay per 64-row block.
+template <bool FP8, int XS_K, int BH, int RPW>
 struct LmqShape {
   static constexpr int BROWS = 16 * BH;              // batch rows per pass: 32 or 64
   static constexpr int WIN_K = FP8 ? 256 : 128;      // K values per window (256 bytes of a row)
   static constexpr int WPS = XS_K / 2 / WIN_K;       // windows per slice per wave
   static constexpr int XBYTES = BROWS * XS_K * 2;    // one x buffer
   static constexpr int XCH = XBYTES / 16 / 512;      // 16-byte x chunks per thread per slice
-  static constexpr int STAGE = 16 * 256;             // one wave's window in LDS
+  static constexpr int STAGE = 16 * 256 * RPW;       // one wave's windows in LDS
   static constexpr int LDS = 2 * XBYTES + 8 * STAGE;
-  static_assert(WPS >= 1 && XCH >= 1 && LDS <= 160 * 1024, "row-quad shape");
+  static_assert(WPS >= 1 && XCH >= 1 && LDS <= 160 * 1024 && (RPW == 1 || RPW == 2), "row-quad shape");
 };
 
-template <bool FP8, int XS_K, int D, int NXS, bool ROT, int BH>
+template <bool FP8, int XS_K, int D, int NXS, bool ROT, int BH, int RPW>
 __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int n_tiles, int b0) {
-  using SH = LmqShape<FP8, XS_K, BH>;
+  using SH = LmqShape<FP8, XS_K, BH, RPW>;
   constexpr int WIN_K = SH::WIN_K, WPS = SH::WPS, XROW = XS_K * 2, XCH = SH::XCH;
   static_assert(D >= 1 && D <= NXS * WPS, "NXS x register sets allow D <= NXS windows per slice");
   __shared__ __attribute__((aligned(16))) unsigned char lds[SH::LDS];
@@ -838,7 +843,7 @@ __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.K, V = p.V;
   const int nbatch = min(SH::BROWS, p.B - b0);
-  const int tile = blockIdx.x, row0 = tile * 64;
+  const int tile = blockIdx.x, row0 = tile * 64 * RPW;
   const int g = wave & 3, hk = wave >> 2;
   const int r16 = lane & 15, q = lane >> 4;
   const int nslice = K / XS_K, nw = nslice * WPS;
@@ -847,35 +852,48 @@ __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int 
   unsigned char* const xs = lds;                                  // [2][BROWS][XS_K] bf16
   unsigned char* const stage = lds + 2 * SH::XBYTES + wave * SH::STAGE;
 
-  // Load layout: lane l of quad j reads row 16 g + 4 j + l / 16 (a row past V reads row V - 1;
-  // its outputs are never stored) at bytes 16 (l % 16) of the window.
-  const unsigned char* wq[4];
+  // Load layout: lane l of quad j in block i reads row 64 i + 16 g + 4 j + l / 16 (a row past V
+  // reads row V - 1; its outputs are never stored) at bytes 16 (l % 16) of the window.
+  const unsigned char* wq[RPW][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = min(row0 + 16 * g + 4 * j + q, V - 1);
-    wq[j] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)row * (FP8 ? K : 2 * K) + 16 * r16;
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = min(row0 + 64 * i + 16 * g + 4 * j + q, V - 1);
+      wq[i][j] = reinterpret_cast<const unsigned char*>(p.w) + (int64_t)row * (FP8 ? K : 2 * K) + 16 * r16;
+    }
+  // Operand layout: lane l holds row 64 i + 16 g + l % 16 of block i.
+  bool rok[RPW];
+  const float* srow[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int myrow = row0 + 64 * i + 16 * g + r16;
+    rok[i] = myrow < V;
+    srow[i] = FP8 ? p.wscale + (int64_t)min(myrow, V - 1) * nkb : nullptr;
   }
-  // Operand layout: lane l holds row 16 g + l % 16.
-  const int myrow = row0 + 16 * g + r16;
-  const bool rok = myrow < V;
-  const float* srow = FP8 ? p.wscale + (int64_t)min(myrow, V - 1) * nkb : nullptr;
 
   auto slice_of = [&](int si) { return si + rot < nslice ? si + rot : si + rot - nslice; };
   // first K value of this wave's window wi
   auto win_k = [&](int wi) { return slice_of(wi / WPS) * XS_K + hk * (XS_K / 2) + (wi % WPS) * WIN_K; };
 
   struct Win {
-    u32x4_t w[4];
-    float sc[2];
+    u32x4_t w[RPW][4];
+    float sc[RPW][2];
   };
   auto wload = [&](int wi, Win& r) {
     const int k = win_k(wi);
     const int64_t off = FP8 ? (int64_t)k : 2 * (int64_t)k;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.w[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wq[j] + off));
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r.w[i][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wq[i][j] + off));
     if constexpr (FP8) {
-      r.sc[0] = srow[k / 128];
-      r.sc[1] = srow[k / 128 + 1];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        r.sc[i][0] = srow[i][k / 128];
+        r.sc[i][1] = srow[i][k / 128 + 1];
+      }
     }
   };
   // x slice si (in visiting order): thread chunk j is chunk tid + 512 j of the [BROWS][XS_K]
@@ -899,28 +917,35 @@ __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int 
     }
   };
 
-  f32x4_t acc[BH], part[BH];
-  static_for<BH>([&](auto h) {
-    static_for<4>([&](auto v) {
-      acc[h][decltype(v)::value] = 0.0f;
-      part[h][decltype(v)::value] = 0.0f;
+  f32x4_t acc[RPW][BH], part[RPW][BH];
+  static_for<RPW>([&](auto i) {
+    static_for<BH>([&](auto h) {
+      static_for<4>([&](auto v) {
+        acc[i][h][decltype(v)::value] = 0.0f;
+        part[i][h][decltype(v)::value] = 0.0f;
+      });
     });
   });
 
   auto compute = [&](const Win& r, int buf, int w2) {
-    // the window through this wave's LDS stage: row R's chunk C at chunk C ^ R
+    // each block's window through this wave's LDS stage (4 KB per block): row R's chunk C at
+    // chunk C ^ R
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 4 * j + q;
-      *reinterpret_cast<u32x4_t*>(stage + row * 256 + ((r16 ^ row) << 4)) = r.w[j];
-    }
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * j + q;
+        *reinterpret_cast<u32x4_t*>(stage + i * 4096 + row * 256 + ((r16 ^ row) << 4)) = r.w[i][j];
+      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    u32x4_t wf[4];
+    u32x4_t wf[RPW][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      wf[t] = *reinterpret_cast<const u32x4_t*>(stage + r16 * 256 + (((4 * t + q) ^ r16) << 4));
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        wf[i][t] = *reinterpret_cast<const u32x4_t*>(stage + i * 4096 + r16 * 256 + (((4 * t + q) ^ r16) << 4));
     const unsigned char* xb = xs + buf * SH::XBYTES;
     const int cx0 = hk * (XS_K / 16) + w2 * (WIN_K / 8);  // the window's first x chunk
     auto xfrag = [&](int hb, int c) {
@@ -932,33 +957,42 @@ __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int 
       if constexpr (FP8) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint32_t lo = h ? wf[t][2] : wf[t][0], hi = h ? wf[t][3] : wf[t][1];
-          u32x4_t wv;
-          wv[0] = e4m3x2_to_bf16x2<false>(lo);
-          wv[1] = e4m3x2_to_bf16x2<true>(lo);
-          wv[2] = e4m3x2_to_bf16x2<false>(hi);
-          wv[3] = e4m3x2_to_bf16x2<true>(hi);
-          const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wv);
           const int c = cx0 + 8 * t + 2 * q + h;
-          static_for<BH>([&](auto hb) {
-            part[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xfrag(hb, c), wb, part[hb], 0, 0, 0);
+          bf16x8_t xf[BH];
+          static_for<BH>([&](auto hb) { xf[hb] = xfrag(hb, c); });
+          static_for<RPW>([&](auto i) {
+            const uint32_t lo = h ? wf[i][t][2] : wf[i][t][0], hi = h ? wf[i][t][3] : wf[i][t][1];
+            u32x4_t wv;
+            wv[0] = e4m3x2_to_bf16x2<false>(lo);
+            wv[1] = e4m3x2_to_bf16x2<true>(lo);
+            wv[2] = e4m3x2_to_bf16x2<false>(hi);
+            wv[3] = e4m3x2_to_bf16x2<true>(hi);
+            const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wv);
+            static_for<BH>([&](auto hb) {
+              part[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[hb], wb, part[i][hb], 0, 0, 0);
+            });
           });
         }
         if constexpr (t % 2 == 1) {  // a 128-wide block is complete: scale it into the sum
-          const float sc = rok ? r.sc[t / 2] : 0.0f;
-          static_for<BH>([&](auto hb) {
-            static_for<4>([&](auto v) {
-              constexpr int vv = v;
-              acc[hb][vv] = fmaf(part[hb][vv], sc, acc[hb][vv]);
-              part[hb][vv] = 0.0f;
+          static_for<RPW>([&](auto i) {
+            const float sc = rok[i] ? r.sc[i][t / 2] : 0.0f;
+            static_for<BH>([&](auto hb) {
+              static_for<4>([&](auto v) {
+                constexpr int vv = v;
+                acc[i][hb][vv] = fmaf(part[i][hb][vv], sc, acc[i][hb][vv]);
+                part[i][hb][vv] = 0.0f;
+              });
             });
           });
         }
       } else {
-        const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wf[t]);
         const int c = cx0 + 4 * t + q;
         static_for<BH>([&](auto hb) {
-          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xfrag(hb, c), wb, acc[hb], 0, 0, 0);
+          const bf16x8_t xf = xfrag(hb, c);
+          static_for<RPW>([&](auto i) {
+            const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, wf[i][t]);
+            acc[i][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, wb, acc[i][hb], 0, 0, 0);
+          });
         });
       }
     });
@@ -998,8 +1032,16 @@ __global__ __launch_bounds__(512) void lm_head_quad_kernel(LmHeadProblem p, int 
   int base = 0;
   for (; base < nw - PER; base += PER) period(base, std::false_type{});
   period(base, std::true_type{});
-  // the last window ended a slice: every wave passed that barrier, the x buffers are free
-  lm_tile64_finish<BH>(p, acc, reinterpret_cast<float*>(xs), n_tiles, b0, nbatch);
+  // the last window ended a slice: every wave passed that barrier, the x buffers are free.
+  // Block i is 64-row tile RPW tile + i; a second block past the shard's last tile has no rows.
+  static_for<RPW>([&](auto i) {
+    constexpr int ii = i;
+    const int t64 = tile * RPW + ii;
+    if (t64 < n_tiles) {
+      if constexpr (ii > 0) __syncthreads();  // the previous block's reads of the buffer are done
+      lm_tile64_finish<BH>(p, acc[ii], reinterpret_cast<float*>(xs), n_tiles, b0, nbatch, t64);
+    }
+  });
 }
 
 // Reduces every workgroup's (max, lowest index) candidate of one batch row (one workgroup
@@ -1149,14 +1191,15 @@ int xres_pass_rows(const LmHeadProblem& p) { return p.B <= 32 ? 32 : 64; }
 // Row-quad kernel. Shapes kLmQuadShape + i take variant i: x slice width, windows in flight,
 // x register sets, staggered slice order, 16-row batch groups per pass; for bf16 and E4M3.
 struct LmQuadCfg {
-  int xs_k, d, nxs, rot, bh;
+  int xs_k, d, nxs, rot, bh, rpw;
 };
-constexpr int kLmQuadCount = 5;
+constexpr int kLmQuadCount = 6;
 constexpr LmQuadCfg kLmQuad[kLmQuadCount][2] = {
-    {{256, 2, 2, 1, 2}, {1024, 2, 2, 1, 2}},  // the default up to 32 batch rows
-    {{256, 2, 2, 1, 4}, {512, 2, 2, 1, 4}},   // the default above: 64-row passes
-    {{256, 4, 4, 1, 2}, {512, 4, 4, 1, 2}},   {{512, 4, 2, 1, 2}, {512, 2, 2, 1, 2}},
-    {{512, 2, 2, 1, 4}, {512, 1, 1, 1, 4}}};
+    {{256, 2, 2, 1, 2, 1}, {1024, 2, 2, 1, 2, 1}},  // the default up to 32 batch rows
+    {{256, 2, 2, 1, 4, 1}, {512, 2, 2, 1, 4, 1}},   // the default above: 64-row passes
+    {{256, 4, 4, 1, 2, 1}, {512, 4, 4, 1, 2, 1}},   {{512, 4, 2, 1, 2, 1}, {512, 2, 2, 1, 2, 1}},
+    {{512, 2, 2, 1, 4, 1}, {512, 1, 1, 1, 4, 1}},
+    {{256, 2, 2, 1, 2, 2}, {512, 2, 2, 1, 2, 2}}};  // 128 rows per workgroup
 bool is_quad(int shape) { return shape >= kLmQuadShape && shape < kLmQuadShape + kLmQuadCount; }
 int quad_pass_rows(const LmHeadProblem& p, int shape) { return 16 * kLmQuad[shape - kLmQuadShape][p.w_fp8 ? 1 : 0].bh; }
 // K must hold whole periods of windows (see lm_head_quad_kernel).
@@ -1169,9 +1212,9 @@ bool quad_ok(const LmHeadProblem& p, int shape) {
 template <bool FP8, int I>
 void launch_quad(const LmHeadProblem& p, int b0, hipStream_t stream) {
   constexpr LmQuadCfg c = kLmQuad[I][FP8];
-  const int n_tiles = (p.V + 63) / 64;
-  hipLaunchKernelGGL((lm_head_quad_kernel<FP8, c.xs_k, c.d, c.nxs, c.rot != 0, c.bh>), dim3(n_tiles), dim3(512), 0,
-                     stream, p, n_tiles, b0);
+  const int n_tiles = (p.V + 63) / 64;  // 64-row tiles: one argmax candidate each
+  hipLaunchKernelGGL((lm_head_quad_kernel<FP8, c.xs_k, c.d, c.nxs, c.rot != 0, c.bh, c.rpw>),
+                     dim3((n_tiles + c.rpw - 1) / c.rpw), dim3(512), 0, stream, p, n_tiles, b0);
   hipLaunchKernelGGL(lm_head_argmax_kernel, dim3(min(16 * c.bh, p.B - b0)), dim3(LM_FIN_THREADS), 0, stream, p, n_tiles,
                      b0, 16 * c.bh);
 }
@@ -1215,6 +1258,7 @@ void launch_any(const LmHeadProblem& p, int shape, int b0, hipStream_t stream) {
     case kLmQuadShape + 2: launch_quad<FP8, 2>(p, b0, stream); break;
     case kLmQuadShape + 3: launch_quad<FP8, 3>(p, b0, stream); break;
     case kLmQuadShape + 4: launch_quad<FP8, 4>(p, b0, stream); break;
+    case kLmQuadShape + 5: launch_quad<FP8, 5>(p, b0, stream); break;
     case 1: launch_shape<FP8, 1>(p, b0, stream); break;
     case 2: launch_shape<FP8, 2>(p, b0, stream); break;
     case 3: launch_shape<FP8, 3>(p, b0, stream); break;

@@ -227,7 +227,7 @@ def test_lm_head_x_resident_slices_and_batch_passes(fp8, B, K, vocab):
         tt.set_lm_head_shape(-1)
 
 
-@pytest.mark.parametrize("shape", [11, 12, 13, 14, 15])
+@pytest.mark.parametrize("shape", [11, 12, 13, 14, 15, 16])
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("B,K,vocab,tp", [(32, 2048, 8013, 8), (7, 4096, 201, 2), (40, 2048, 258, 2),
                                           (70, 4096, 8013, 8)])
