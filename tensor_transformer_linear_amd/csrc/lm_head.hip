@@ -820,7 +820,9 @@ constexpr int lm_lcm(int a, int b) { return a / lm_gcd(a, b) * b; }
 // RPW = 2: the workgroup owns two 64-row blocks (128 rows) and wave w multiplies row group g in
 // both, rows 16 g and 64 + 16 g of the workgroup's rows, so every x fragment a wave reads from
 // LDS feeds two MFMAs and each workgroup's x slices serve twice the weight bytes. A window is
-// then one 16-row window per block (eight loads); candidates stay per 64-row block.
+// then one 16-row window per block (eight loads); candidates stay per 64-row block. A tuning
+// shape only: on the decode shard its 126 workgroups leave half the CUs idle, and a CU streams no
+// faster with the extra rows (1.5x the 64-row kernel's time).
 template <bool FP8, int XS_K, int BH, int RPW>
 struct LmqShape {
   static constexpr int BROWS = 16 * BH;              // batch rows per pass: 32 or 64
