@@ -1197,9 +1197,9 @@ struct LmQuadCfg {
 };
 constexpr int kLmQuadCount = 6;
 constexpr LmQuadCfg kLmQuad[kLmQuadCount][2] = {
-    {{256, 2, 2, 1, 2, 1}, {1024, 2, 2, 1, 2, 1}},  // the default up to 32 batch rows
+    {{256, 2, 2, 1, 2, 1}, {512, 2, 2, 1, 2, 1}},   // the default up to 32 batch rows
     {{256, 2, 2, 1, 4, 1}, {512, 2, 2, 1, 4, 1}},   // the default above: 64-row passes
-    {{256, 4, 4, 1, 2, 1}, {512, 4, 4, 1, 2, 1}},   {{512, 4, 2, 1, 2, 1}, {512, 2, 2, 1, 2, 1}},
+    {{256, 4, 4, 1, 2, 1}, {512, 4, 4, 1, 2, 1}},   {{512, 4, 2, 1, 2, 1}, {1024, 2, 2, 1, 2, 1}},
     {{512, 2, 2, 1, 4, 1}, {512, 1, 1, 1, 4, 1}},
     {{256, 2, 2, 1, 2, 2}, {512, 2, 2, 1, 2, 2}}};  // 128 rows per workgroup
 bool is_quad(int shape) { return shape >= kLmQuadShape && shape < kLmQuadShape + kLmQuadCount; }
@@ -1229,7 +1229,8 @@ int effective_shape(const LmHeadProblem& p, int shape) {
 
 // The default launch shape: the row-quad kernel, in 32-row batch passes up to 32 rows and in
 // 64-row passes above, which stream the weight once per 64 rows. On the decode workload (K 4096,
-// 16032 rows; kernel times from a HIP kernel trace): 32 rows 25.1 us bf16 and 20.2 us E4M3,
+// 16032 rows; kernel times from a HIP kernel trace): 32 rows 25.1 us bf16 and 19.7 us E4M3
+// (512-wide x slices for E4M3: 0.4-0.5 us under 1024-wide ones in four interleaved rounds),
 // against 30.3 and 24.3 us for the LDS ring; 64 rows in one pass 30.8 and 28.9 us, against
 // 40.2 and 32.7 us for the x-resident kernel. A K that the row-quad kernel cannot take runs the
 // x-resident kernel above 32 rows if it can, else the LDS ring.

@@ -312,12 +312,12 @@ def test_lm_head_special_values(shape, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("B,K,vocab,tp", [(1, 512, 40, 1), (33, 2048, 1000, 2), (64, 4096, 700, 1), (65, 2048, 300, 1),
-                                          (5, 1536, 300, 1)])
+@pytest.mark.parametrize("B,K,vocab,tp", [(1, 512, 40, 1), (3, 1024, 130, 1), (33, 2048, 1000, 2), (64, 4096, 700, 1),
+                                          (65, 2048, 300, 1), (5, 1536, 300, 1)])
 def test_lm_head_default_shape_edges(fp8, B, K, vocab, tp):
     """The default launch choice at its edges: one row over a shard shorter than one 64-row tile,
     33 and 64 rows (one 64-row pass), 65 rows (a second pass of one row), the smallest K the
-    row-quad kernel takes (512 bf16; 2048 E4M3), and K 1536, which the E4M3 row-quad kernel does
+    row-quad kernel takes (512 bf16; 1024 E4M3), and K 1536, which the E4M3 row-quad kernel does
     not take (the LDS ring runs instead)."""
     lg, idx, mx, ref = _lm_case(B, K, vocab, tp, 0, 64, 170 + B, fp8)
     assert argmax_ok(idx.cpu().numpy(), ref) == []
