@@ -85,6 +85,7 @@ TUNING_SIGNATURES = {
     "tpt_gemm_fp8_pick_tile": (_int, [_i64, _i64, _i64]),
     "tpt_lm_head_shape_count": (_int, []),
     "tpt_mfma_row_sums": (_int, [_int, _vp, _vp, _vp, _vp]),
+    "tpt_rmsnorm_rows": (_int, [_vp, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "tpt_stream_probe": (_int, [_int, _int, _vp, _i64, _vp, _vp]),
     "tpt_mfma_rate": (_int, [_int, _int, _int, _vp, _vp]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -472,6 +473,24 @@ def rmsnorm_column_linear(x, scale, eps, w_shard, bias_shard, subparam_sizes, tp
           _ptr(bias_shard), sizes, n, tp_size, rank, _ptr(y), y_dtype, layout, ldy, _ptr(workspace),
           workspace.numel(), _stream(stream))
     return y
+
+
+def rmsnorm_rows(x, scale, eps, xnorm_out, workspace, stream=None):
+    """The RMSNorm pass of ``rmsnorm_column_linear`` alone, into ``xnorm_out`` (tuning library;
+    for measurements that time the column GEMM as the full call runs it)."""
+    _tensor(x, "x", _BF16, (None, None))
+    M, K = x.shape
+    if scale is not None:
+        _tensor(scale, "scale", _BF16, (K,))
+    _tensor(xnorm_out, "xnorm_out", _BF16, (M, K))
+    _tensor(workspace, "workspace", (torch.uint8,))
+    _same_gpu(x=x, scale=scale, xnorm_out=xnorm_out, workspace=workspace)
+    l = tuning_lib()
+    st = l.tpt_rmsnorm_rows(_ptr(x), M, K, _ptr(scale), float(eps), _ptr(xnorm_out), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    if st != TP_OK:
+        raise TpError(st, l.tp_last_error().decode())
+    return xnorm_out
 
 
 def tp_lm_head_workspace_bytes(B, vocab, tp_size, rank) -> int:

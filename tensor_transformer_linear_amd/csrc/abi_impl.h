@@ -46,6 +46,11 @@ int lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int
                          float* logits, int32_t* argmax_local, float* max_logit, void* workspace,
                          size_t workspace_bytes, void* stream, const Tuning& tune);
 
+// The RMSNorm pass of rmsnorm_column_linear alone: r and t into the workspace, the normalised
+// rows into xnorm_out (which must be non-NULL).
+int rmsnorm_rows(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 // Validates a tuning choice; sets the calling thread's message and returns a status.
 int check_tuning(const Tuning& tune);
 

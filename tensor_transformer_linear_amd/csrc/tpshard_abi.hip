@@ -328,6 +328,31 @@ int o_wo_partial(const void* y_fused, int64_t M, int64_t heads, int64_t padded_h
   return hip_status(tpk::launch_gemm(p, tune.tile, tune.path, as_stream(stream)), "tp_o_wo_partial launch");
 }
 
+int rmsnorm_rows(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (x == nullptr || xnorm_out == nullptr || workspace == nullptr)
+    return fail(TP_ERR_INVALID_ARG, "x, xnorm_out and workspace must be non-NULL");
+  if (M < 0 || K < 1) return fail(TP_ERR_INVALID_ARG, "M = %lld must be >= 0 and K = %lld >= 1", (long long)M,
+                                  (long long)K);
+  if (M > INT_MAX || K > INT_MAX) return fail(TP_ERR_UNSUPPORTED, "sizes must fit in 31 bits");
+  if (K % 8) return fail(TP_ERR_UNSUPPORTED, "K = %lld must be a multiple of 8", (long long)K);
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(TP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!aligned(x, 16) || !aligned(xnorm_out, 16) || (scale != nullptr && !aligned(scale, 16)))
+    return fail(TP_ERR_UNSUPPORTED, "x, xnorm_out and scale must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t need = tp_rmsnorm_workspace_min_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(TP_ERR_SHAPE, "workspace has %zu bytes, at least %zu needed", workspace_bytes, need);
+  if (M == 0) return ok();
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* r = reinterpret_cast<float*>(ws);
+  uint16_t* t = reinterpret_cast<uint16_t*>(ws + align_up((size_t)M * 4, 256));
+  return hip_status(tpk::launch_rmsnorm_rows(static_cast<const uint16_t*>(x), (int)M, (int)K,
+                                             static_cast<const uint16_t*>(scale), eps, r, scale ? t : nullptr,
+                                             static_cast<uint16_t*>(xnorm_out), as_stream(stream)),
+                    "rmsnorm rows launch");
+}
+
 int rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
                           const void* w_shard, const void* bias_shard, const int64_t* subparam_sizes, int n_sub,
                           int tp_size, int rank, void* y, int y_dtype, int layout, int64_t ldy, void* workspace,

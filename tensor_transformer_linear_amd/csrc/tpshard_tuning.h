@@ -51,6 +51,12 @@ TP_API int tpt_lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t
                                     const float* w_block_scale, float* logits, int32_t* argmax_local,
                                     float* max_logit, void* workspace, size_t workspace_bytes, void* stream,
                                     int lm_shape);
+/* The RMSNorm pass of rmsnorm_column_linear alone (no GEMM): the same arguments, xnorm_out
+ * required, the workspace at least tp_rmsnorm_workspace_min_bytes(M, K). For measurements that
+ * time the column GEMM under the conditions of the full call (the pass runs just before it). */
+TP_API int tpt_rmsnorm_rows(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* The automatic tile for an M x N x K bf16 GEMM and for an E4M3 one (-1 for invalid sizes),
  * and the number of LM-head launch shapes. */
 TP_API int tpt_gemm_pick_tile(int64_t M, int64_t N, int64_t K);

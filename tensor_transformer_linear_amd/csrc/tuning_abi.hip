@@ -75,6 +75,11 @@ TP_API int tpt_rmsnorm_column_linear(const void* x, int64_t M, int64_t K, const 
                                       tp_size, rank, y, y_dtype, layout, ldy, workspace, workspace_bytes, stream, t);
 }
 
+TP_API int tpt_rmsnorm_rows(const void* x, int64_t M, int64_t K, const void* scale, float eps, void* xnorm_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return tpabi::rmsnorm_rows(x, M, K, scale, eps, xnorm_out, workspace, workspace_bytes, stream);
+}
+
 TP_API int tpt_lm_head_shard_argmax(const void* x, int64_t B, int64_t K, int64_t vocab, int tp_size, int rank,
                                     int64_t max_rows_per_chunk, const void* w_shard, int w_dtype,
                                     const float* w_block_scale, float* logits, int32_t* argmax_local,

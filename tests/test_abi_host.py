@@ -257,6 +257,22 @@ def test_stream_probe_host_checks():
     assert T.tpt_mfma_rate(0, 8, 10, None, None) == tt.TP_ERR_INVALID_ARG
 
 
+def test_rmsnorm_rows_host_checks():
+    # the RMSNorm-only measurement call refuses bad arguments on the host, before any launch
+    T = tt.tuning_lib()
+    need = tt.lib().tp_rmsnorm_workspace_min_bytes(64, 128)
+    assert T.tpt_rmsnorm_rows(A, 64, 128, None, 1e-6, None, WS, need, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_rmsnorm_rows(None, 64, 128, None, 1e-6, A2, WS, need, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_rmsnorm_rows(A, 64, 0, None, 1e-6, A2, WS, need, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_rmsnorm_rows(A, 64, 124, None, 1e-6, A2, WS, need, None) == tt.TP_ERR_UNSUPPORTED
+    assert T.tpt_rmsnorm_rows(A, 64, 128, None, -1.0, A2, WS, need, None) == tt.TP_ERR_INVALID_ARG
+    assert T.tpt_rmsnorm_rows(A, 64, 128, None, 1e-6, A2, WS, need - 1, None) == tt.TP_ERR_SHAPE
+    assert b"workspace" in T.tp_last_error()
+    assert T.tpt_rmsnorm_rows(A, 64, 128, None, 1e-6, ctypes.c_void_p(0x20008), WS, need, None) == \
+        tt.TP_ERR_UNSUPPORTED
+    assert T.tpt_rmsnorm_rows(A, 0, 128, None, 1e-6, A2, WS, need, None) == tt.TP_OK  # nothing to do
+
+
 def test_tuning_routing_restores_the_product_library():
     assert getattr(tt._tls, "choices", None) is None
     with tt.tuning(tile=3):

@@ -36,6 +36,10 @@ def test_rmsnorm_column_linear(K, scaled):
     # the fused A-load normalisation computes the same bf16 operand as the materialised rows
     assert torch.equal(y_mat.view(torch.int16), y_fused.view(torch.int16))
     assert torch.equal(y_mat.view(torch.int16), y_ws.view(torch.int16))
+    # the RMSNorm pass alone (the tuning library's measurement call) writes the same rows
+    xn2 = torch.full((M, K), 7.0, dtype=torch.bfloat16, device="cuda")
+    tt.rmsnorm_rows(X, S, 1e-6, xn2, small)
+    assert torch.equal(xn.view(torch.int16), xn2.view(torch.int16))
 
 
 def test_rmsnorm_special_rows():
