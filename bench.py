@@ -366,7 +366,7 @@ def measured_traffic():
         return None
 
 
-LEG_WARMUP = 10  # untimed launches before the roofline leg's timed ones
+LEG_WARMUP = 30  # untimed calls before each leg's timed ones
 
 
 def roofline_leg(wl, launches, stream):
@@ -393,27 +393,32 @@ def roofline_leg(wl, launches, stream):
     else:
         return None
 
-    def timed(with_pre):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
-        torch.cuda.synchronize()
+    def events():
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+
+    def timed(evs, with_pre):
         for a, b in evs:
             if with_pre:
                 pre()
             a.record(stream)
             launch()
             b.record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
 
-    # Untimed warm-up: the first launches after the step loop's final synchronize run up to 30%
-    # slower while the power controller settles (kernel traces show it), unlike the launches
-    # inside the timed steps.
+    evs, evs_b2b = events(), events()
+    torch.cuda.synchronize()
+    # Untimed warm-up, with no synchronize between it and the timed launches: the first
+    # launches after an idle moment run up to 40% slower while the power controller settles
+    # (kernel traces show it), unlike the launches inside the timed steps.
     for _ in range(LEG_WARMUP):
         if pre is not None:
             pre()
         launch()
-    us = timed(pre is not None)
-    us_b2b = timed(False) if pre is not None else us
+    timed(evs, pre is not None)
+    if pre is not None:
+        timed(evs_b2b, False)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    us_b2b = float(np.mean([a.elapsed_time(b) for a, b in evs_b2b])) * 1e3 if pre is not None else us
     ach = flops / (us * 1e-6) / 1e12
     traffic = measured_traffic() if key == 4 else None
     out = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -464,10 +469,10 @@ def fp8_prefill_leg(launches, stream):
         if ev is not None:
             ev[2].record(stream)
 
-    run()
-    run()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
     torch.cuda.synchronize()
+    for _ in range(LEG_WARMUP):  # past the power controller's settling transient, no synchronize after
+        run()
     for ev in evs:
         run(ev)
     torch.cuda.synchronize()
@@ -519,10 +524,10 @@ def swiglu_leg(launches, stream):
         if ev is not None:
             ev[2].record(stream)
 
-    run()
-    run()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
     torch.cuda.synchronize()
+    for _ in range(LEG_WARMUP):  # past the power controller's settling transient, no synchronize after
+        run()
     for ev in evs:
         run(ev)
     torch.cuda.synchronize()
@@ -608,10 +613,10 @@ def embedding_leg(launches, stream):
     tok = torch.from_numpy(synth.rng(6, 0).integers(0, vocab, n).astype(np.int32)).to(dev)
     out = torch.empty((n, E), dtype=torch.bfloat16, device=dev)
     hits = int(((tok >= 0) & (tok < rows)).sum().item())
-    for _ in range(2):
-        tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
     torch.cuda.synchronize()
+    for _ in range(LEG_WARMUP):  # no synchronize between the warm-up and the timed launches
+        tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
     for a, b in evs:
         a.record(stream)
         tt.tp_vocab_embedding(tok, vocab, tp, rank, tbl, out)
